@@ -1,0 +1,182 @@
+"""Plain Python reference of the step's host metadata (FIFO fill, page allocation, ragged metadata).
+
+Test infrastructure only: the product never imports it; it shares no code with the C++ scheduler it checks.
+
+Rules followed (Transformers "continuous batching architecture" page, sections "调度器"/"FIFO"/"准入"/"内存管理";
+"Continuous Batching" blog, languisher.top, sections "扩展：vLLM v1 中的实现" and "扩展：与 Chunked Prefill 结合"):
+
+* A forward pass takes at most `max_batch_tokens` query tokens and `max_requests` requests.
+* FIFO order: first the active decodes (one token each), then the active prefills (continuing chunks), then the
+  waiting requests in arrival order. A prompt longer than the budget left is cut; the rest waits for the next step.
+* Admission of a waiting request is all-or-nothing across the layer types: if any allocator lacks the pages, nothing
+  is allocated and the request is rejected. Reading: admission stops at the first rejection (no skipping ahead).
+* While the free fraction of any pool is below `safety_margin`, new prefills are held (decodes continue).
+* Reading for active requests that need pages no pool can give: they are reported stalled and left out of the step.
+* Pages come from the front of each layer's free list. Full layers add pages as the sequence grows; a sliding layer
+  gives each request a fixed ring of `ring_len` pages at admission.
+* Metadata: query_start_loc [N+1] (exclusive prefix sum of the query lengths plus the total), seq_lens [N]
+  (context + this step's tokens), block_table [N, width] padded with the padding page, slot_mapping [T].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+DECODING, PREFILLING, WAITING = 0, 1, 2
+OK, E_INVAL, E_NOSPACE = "ok", "inval", "nospace"
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def ring_is_large_enough(ring_len, window_left, max_chunk, page_size):
+    """A ring must hold every key still visible to this step's queries plus the keys the step appends.
+
+    Queries at ctx..ctx+q-1 see back to ctx-window_left, so window_left+q consecutive positions must map to distinct
+    ring slots; with arbitrary alignment they span at most (window_left+q+page_size-2)//page_size + 1 pages.
+    """
+    return ring_len >= (window_left + max_chunk + page_size - 2) // page_size + 1
+
+
+def build_metadata(requests, layers, max_batch_tokens, max_requests, page_size, safety_margin=0.0, pad_page=0):
+    """Schedule one step.
+
+    requests: sequence with .state, .num_computed, .num_pending, .pages (list per layer), in arrival order.
+    layers: sequence of dicts {ring_len, window_left, pool_pages, free_pages}.
+    Returns a dict (see module docstring); "status" is "ok", "inval" or "nospace".
+    """
+    P = page_size
+    L = len(layers)
+    if P < 1 or max_batch_tokens < 1 or max_requests < 1 or L < 1:
+        return {"status": E_INVAL}
+    for lay in layers:
+        if lay["ring_len"] > 0:
+            if lay["window_left"] < 0 or not ring_is_large_enough(lay["ring_len"], lay["window_left"],
+                                                                   max_batch_tokens, P):
+                return {"status": E_INVAL}
+    for rq in requests:
+        if rq.num_computed < 0 or rq.num_pending < 1 or rq.state not in (DECODING, PREFILLING, WAITING):
+            return {"status": E_INVAL}
+        if rq.state == DECODING and rq.num_pending != 1:
+            return {"status": E_INVAL}
+        for l, lay in enumerate(layers):
+            owned = len(rq.pages[l])
+            if lay["ring_len"] > 0:
+                if rq.state != WAITING and owned != lay["ring_len"]:
+                    return {"status": E_INVAL}
+            elif owned < _cdiv(rq.num_computed, P):
+                return {"status": E_INVAL}
+
+    free = [np.asarray(lay["free_pages"], dtype=np.int32) for lay in layers]
+    taken = [0] * L
+
+    def needs(rq, q):
+        out = []
+        for l, lay in enumerate(layers):
+            have = len(rq.pages[l])
+            if lay["ring_len"] > 0:
+                out.append(max(0, lay["ring_len"] - have))
+            else:
+                out.append(max(0, _cdiv(rq.num_computed + q, P) - have))
+        return out
+
+    def fits(nd):
+        return all(nd[l] <= len(free[l]) - taken[l] for l in range(L))
+
+    def take(nd):
+        got = []
+        for l in range(L):
+            got.append(free[l][taken[l]:taken[l] + nd[l]].copy())
+            taken[l] += nd[l]
+        return got
+
+    rows = []          # (request index, q_len, new pages per layer)
+    stalled = []
+    first_rejected = -1
+    held = False
+    budget = max_batch_tokens
+
+    # 1) active decodes, one token each
+    for i, rq in enumerate(requests):
+        if rq.state != DECODING:
+            continue
+        if len(rows) >= max_requests or budget < 1:
+            break
+        nd = needs(rq, 1)
+        if not fits(nd):
+            stalled.append(i)
+            continue
+        rows.append((i, 1, take(nd)))
+        budget -= 1
+    num_decodes = len(rows)
+
+    # 2) active prefills, continuing where they stopped
+    for i, rq in enumerate(requests):
+        if rq.state != PREFILLING:
+            continue
+        if len(rows) >= max_requests or budget < 1:
+            break
+        q = min(rq.num_pending, budget)
+        nd = needs(rq, q)
+        if not fits(nd):
+            stalled.append(i)
+            continue
+        rows.append((i, q, take(nd)))
+        budget -= q
+
+    # 3) waiting requests in arrival order (admission)
+    for i, rq in enumerate(requests):
+        if rq.state != WAITING:
+            continue
+        if len(rows) >= max_requests or budget < 1:
+            break
+        if any(lay["pool_pages"] > 0 and (len(free[l]) - taken[l]) < safety_margin * lay["pool_pages"]
+               for l, lay in enumerate(layers)):
+            held = True
+            break
+        q = min(rq.num_pending, budget)
+        nd = needs(rq, q)
+        if not fits(nd):
+            first_rejected = i
+            break
+        rows.append((i, q, take(nd)))
+        budget -= q
+
+    N = len(rows)
+    q_lens = np.array([q for _, q, _ in rows], dtype=np.int64)
+    qsl = np.zeros(N + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(q_lens)
+    T = int(qsl[-1])
+    seq_lens = np.array([requests[i].num_computed + q for i, q, _ in rows], dtype=np.int32)
+    req_index = np.array([i for i, _, _ in rows], dtype=np.int32)
+
+    out = {"status": OK, "query_start_loc": qsl, "seq_lens": seq_lens, "req_index": req_index,
+           "num_reqs": N, "num_tokens": T, "num_decodes": num_decodes, "stalled": np.array(stalled, np.int32),
+           "first_rejected": first_rejected, "held_by_margin": held, "layers": []}
+    if N == 0 and (stalled or first_rejected >= 0):
+        out["status"] = E_NOSPACE
+
+    for l, lay in enumerate(layers):
+        R = lay["ring_len"]
+        if R > 0:
+            width = R
+        else:
+            width = max((_cdiv(int(s), P) for s in seq_lens), default=0)
+        table = np.full((N, width), pad_page, dtype=np.int32)
+        slots = np.zeros(T, dtype=np.int32)
+        for r, (i, q, new) in enumerate(rows):
+            rq = requests[i]
+            pages = np.concatenate([np.asarray(rq.pages[l], dtype=np.int32), new[l]]).astype(np.int32)
+            if R > 0:
+                table[r, :] = pages[:R]
+            else:
+                n = _cdiv(int(seq_lens[r]), P)
+                table[r, :n] = pages[:n]
+            for j in range(q):
+                pos = rq.num_computed + j
+                blk, off = pos // P, pos % P
+                phys = table[r, blk % R] if R > 0 else table[r, blk]
+                slots[qsl[r] + j] = phys * P + off
+        out["layers"].append({"block_table": table, "slot_mapping": slots,
+                              "ring_len": np.full(N, R, dtype=np.int32), "used_pages": taken[l], "width": width})
+    return out
