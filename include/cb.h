@@ -1,0 +1,239 @@
+/*
+ * cb.h -- C ABI of the mixed-batch paged attention step of continuous batching, for AMD Instinct MI355X (gfx950).
+ *
+ * One forward step of a continuously batched model holds a ragged concatenation of decode tokens and prefill-chunk
+ * tokens. The scheduler builds the step's metadata on the host (query_start_loc, seq_lens, slot_mapping,
+ * block_table) and the attention kernels only check bounds and map logical key positions to physical pages
+ * ("Continuous Batching" blog, languisher.top, section "扩展：vLLM v1 中的实现"). This library provides:
+ *
+ *   cb_build_metadata   host: FIFO fill under a token budget, page allocation, ragged metadata
+ *   cb_plan_attention   host: split the step into kernel work items (decode splits, prefill tiles, merges)
+ *   cb_kv_append        device: write the step's new K/V rows into the paged cache through slot_mapping
+ *   cb_paged_attention  device: attention of every query row of the step over its request's paged keys
+ *
+ * Conventions shared by all calls
+ *   - Every integer array is int32, row-major, densely packed. Device pointers are plain HIP device addresses;
+ *     host pointers are ordinary process memory. The library never frees or keeps any pointer it is given.
+ *   - A step has N requests ("rows" of the metadata) and T query tokens. Request r owns tokens
+ *     query_start_loc[r] .. query_start_loc[r+1]-1; query_start_loc has N+1 entries, [0] = 0, [N] = T.
+ *   - seq_lens[r] = number of keys of request r after this step = context_len + q_len, where context_len keys were
+ *     computed in earlier steps. Token i of request r sits at position context_len + i and attends keys
+ *     [lo, context_len + i] (inclusive; itself included), lo = 0 for full layers, max(0, pos - window_left) for
+ *     sliding layers.
+ *   - Paging: key position p of request r lives in physical page block_table[r][p / page_size] at offset
+ *     p % page_size; in ring mode (sliding layers) in page block_table[r][(p / page_size) % ring_len[r]].
+ *   - Cache layouts (one tensor per layer for K and one for V, element type = the dtype):
+ *        k_cache  [num_pages][num_kv_heads][page_size][head_dim]   (key rows, head_dim contiguous)
+ *        v_cache  [num_pages][num_kv_heads][head_dim][page_size]   (value columns, page offsets contiguous)
+ *     So one kv head's slice of one page is a single contiguous run of page_size*head_dim elements in each tensor.
+ *   - Q and O are [T][num_q_heads][head_dim]; new K/V rows are [T][num_kv_heads][head_dim]. Query head h reads kv
+ *     head h / (num_q_heads / num_kv_heads).
+ *   - dtype: CB_DTYPE_F32 (float) or CB_DTYPE_BF16 (bfloat16). Attention accumulates in fp32; bf16 outputs are
+ *     rounded to nearest even.
+ *   - Device calls are asynchronous on the given stream (a hipStream_t passed as void*, NULL = the null stream).
+ *     They validate arguments synchronously and return before any launch on error.
+ */
+#ifndef CB_H
+#define CB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CB_ABI_VERSION 1
+
+typedef int32_t cb_status;
+#define CB_OK 0
+#define CB_E_INVAL 1        /* inconsistent arguments (lengths, shapes, metadata)                          */
+#define CB_E_NOSPACE 2      /* cb_build_metadata: nothing could be scheduled for lack of free pages        */
+#define CB_E_CAPACITY 3     /* output buffer too small; the needed size is written back                    */
+#define CB_E_UNSUPPORTED 4  /* valid but not implemented (head_dim, page_size, dtype, head ratio)          */
+#define CB_E_WORKSPACE 5    /* cb_paged_attention: workspace missing or too small                          */
+#define CB_E_HIP 6          /* a HIP runtime call or kernel launch failed                                  */
+
+#define CB_DTYPE_F32 0
+#define CB_DTYPE_BF16 1
+
+/* request states, in the order of the request lifecycle (Transformers "continuous batching architecture" page,
+ * section "请求生命周期"): waiting in the queue, prefilling the prompt in chunks, decoding one token per step. */
+#define CB_DECODING 0
+#define CB_PREFILLING 1
+#define CB_WAITING 2
+
+#define CB_MAX_LAYERS 2     /* attention layer types per step: full, and optionally sliding */
+
+/* ------------------------------------------------------------------------------------------- cb_build_metadata */
+
+/* One request known to the scheduler, given in arrival (FIFO) order. */
+typedef struct cb_req {
+    int64_t id;                          /* caller's id; not interpreted                                         */
+    int32_t state;                       /* CB_DECODING, CB_PREFILLING or CB_WAITING                            */
+    int32_t num_computed;                /* keys already in the cache (context before this step), >= 0          */
+    int32_t num_pending;                 /* tokens to feed: exactly 1 for CB_DECODING, >= 1 otherwise            */
+    int32_t n_pages[CB_MAX_LAYERS];      /* pages already owned per layer type                                   */
+    const int32_t *pages[CB_MAX_LAYERS]; /* host arrays of owned page ids, logical order (full) or ring order    */
+} cb_req;
+
+/* One layer type's page pool. */
+typedef struct cb_layer_pool {
+    int32_t ring_len;          /* 0: full attention, pages grow with the sequence; > 0: sliding layer, each
+                                  request owns a ring of exactly ring_len pages from admission on              */
+    int32_t window_left;       /* sliding layers: keys pos-window_left..pos are visible; -1 for full layers     */
+    int32_t pool_pages;        /* allocatable pages of the pool (denominator of the safety margin)              */
+    int32_t n_free;            /* entries of free_pages                                                         */
+    const int32_t *free_pages; /* host array: free pages in allocation order; pages are taken from the front   */
+} cb_layer_pool;
+
+typedef struct cb_sched_params {
+    int32_t max_batch_tokens;  /* token budget of one forward pass, >= 1                                        */
+    int32_t max_requests;      /* request cap of one forward pass, >= 1                                         */
+    int32_t page_size;         /* tokens per page, >= 1                                                         */
+    int32_t pad_page;          /* page id written into unused block-table entries (a reserved padding page)     */
+    int32_t n_layers;          /* 1 or 2 layer types                                                            */
+    float safety_margin;       /* hold new prefills while any pool's free fraction is below this (0 disables)  */
+} cb_sched_params;
+
+/* Header of the packed int32 buffer cb_build_metadata writes. Offsets count int32 elements from the buffer start;
+ * per scheduled row r (schedule order: decodes, then continuing prefills, then admitted requests): */
+typedef struct cb_step {
+    int32_t num_reqs;                        /* N rows scheduled                                                 */
+    int32_t num_tokens;                      /* T                                                                */
+    int32_t num_decodes;                     /* rows 0..num_decodes-1 are the decodes                            */
+    int32_t max_q_len, max_seq_len;
+    int32_t n_stalled;                       /* active requests left out for lack of pages                       */
+    int32_t first_rejected;                  /* input index of the waiting request refused admission, or -1      */
+    int32_t held_by_margin;                  /* 1 if new prefills were held by the safety margin                 */
+    int32_t used_pages[CB_MAX_LAYERS];       /* pages taken from the front of each free list                     */
+    int32_t table_width[CB_MAX_LAYERS];      /* row stride of each layer's block table                           */
+    int64_t off_query_start_loc;             /* [N+1]                                                            */
+    int64_t off_seq_lens;                    /* [N]                                                              */
+    int64_t off_req_index;                   /* [N] input index of each row                                      */
+    int64_t off_stalled;                     /* [n_stalled] input indices                                        */
+    int64_t off_block_table[CB_MAX_LAYERS];  /* [N][table_width]; unused entries hold pad_page                   */
+    int64_t off_slot_mapping[CB_MAX_LAYERS]; /* [T] page * page_size + offset of each new token's K/V            */
+    int64_t off_ring_len[CB_MAX_LAYERS];     /* [N] ring length per row (0 for full layers)                      */
+    int64_t used;                            /* int32 elements written, or needed when CB_E_CAPACITY            */
+} cb_step;
+
+/*
+ * Schedule one step (Transformers "continuous batching architecture" page, sections "调度器", "FIFO", "准入" and
+ * "分块预填充"; "Continuous Batching" blog, section "扩展：与 Chunked Prefill 结合"):
+ *   1. active decodes in FIFO order, one token each;
+ *   2. active prefills, each continuing with min(num_pending, budget left) tokens;
+ *   3. waiting requests in arrival order: held while a pool's free fraction is below safety_margin; admitted
+ *      all-or-nothing across layer types (pages for the chunk, plus a whole ring for sliding layers); the first
+ *      refusal stops admission.
+ *   Every pass stops at max_requests rows or an exhausted budget. Active requests whose pages cannot be allocated
+ *   are reported stalled and left out.
+ * Pure host function: reads reqs/params/layers, writes `out` (capacity out_capacity int32 elements) and `step`.
+ * Returns CB_OK, CB_E_INVAL (inconsistent input, including a ring too small for max_batch_tokens), CB_E_NOSPACE
+ * (no row could be scheduled because pages ran out; out/step are still valid) or CB_E_CAPACITY (step->used tells
+ * the size needed).
+ */
+cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const cb_sched_params *params,
+                            const cb_layer_pool *layers, int32_t *out, int64_t out_capacity, cb_step *step);
+
+/* ------------------------------------------------------------------------------------------- cb_plan_attention */
+
+typedef struct cb_attn_shape {
+    int32_t num_q_heads;       /* Hq, a multiple of num_kv_heads                                               */
+    int32_t num_kv_heads;      /* Hkv                                                                          */
+    int32_t head_dim;          /* D: 64 or 128                                                                 */
+    int32_t page_size;         /* P: a power of two, 1..256                                                    */
+    int32_t dtype;             /* CB_DTYPE_F32 or CB_DTYPE_BF16                                                */
+    int32_t window_left;       /* -1: full attention; >= 0: sliding window                                     */
+    int32_t decode_split;      /* keys per decode split (a multiple of 64), 0 = chosen by the planner          */
+    int32_t prefill_split;     /* keys per prefill-tile split (a multiple of 64), 0 = chosen by the planner    */
+} cb_attn_shape;
+
+/* Header of the packed int32 plan. Work items (8 int32 each) and merge items (4 int32 each) start at the given
+ * element offsets. */
+typedef struct cb_plan {
+    int32_t n_decode;          /* split-KV decode items (rows with q_len 1, fast kernels)                     */
+    int32_t n_prefill;         /* prefill tile items (rows with q_len > 1, fast kernels)                      */
+    int32_t n_rowwise;         /* per-token items of the general kernel (fp32, or shapes the fast kernels skip)*/
+    int32_t n_combine;         /* output tokens merged from partial results                                    */
+    int32_t n_partials;        /* partial-result slots the workspace must hold                                 */
+    int32_t decode_split, prefill_split, prefill_tokens;  /* the sizes used                                    */
+    int32_t num_tokens;        /* T                                                                            */
+    int32_t max_page_index;    /* largest logical block index any item reads (block_table width check)         */
+    int64_t off_decode, off_prefill, off_rowwise, off_combine;
+    int64_t used;              /* int32 elements written, or needed when CB_E_CAPACITY                        */
+} cb_plan;
+
+/*
+ * Split a step into kernel work items: every query row's visible key range [lo, pos] is cut into splits; a row
+ * with one split is written directly, a row with several gets partial results merged by a final pass. Host only.
+ * query_start_loc [N+1], seq_lens [N] (host); ring_len [N] host array or NULL (full layer).
+ * Returns CB_OK, CB_E_INVAL, CB_E_UNSUPPORTED or CB_E_CAPACITY (plan->used tells the size needed).
+ */
+cb_status cb_plan_attention(const int32_t *query_start_loc, const int32_t *seq_lens, const int32_t *ring_len,
+                            int32_t num_reqs, const cb_attn_shape *shape, int32_t *out, int64_t out_capacity,
+                            cb_plan *plan);
+
+/* ------------------------------------------------------------------------------------------------ cb_kv_append */
+
+/*
+ * For every token t with 0 <= slot_mapping[t] < num_pages*page_size, copy k_new[t] and v_new[t] (all kv heads) into
+ * page slot_mapping[t] / page_size at offset slot_mapping[t] % page_size, bit for bit. Tokens with a negative (or
+ * out-of-pool) slot are skipped. slot_mapping is the scheduler's (Continuous Batching blog, section "扩展：vLLM v1
+ * 中的实现": the scheduler builds slot_mapping with the rest of the metadata). Must be enqueued before
+ * cb_paged_attention of the same step: the step's own keys are read back from the cache.
+ * Device pointers: k_cache, v_cache (layouts above), k_new, v_new [T][Hkv][D], d_slot_mapping [T].
+ * Two tokens with the same slot race (last writer wins, unspecified which).
+ */
+cb_status cb_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                       const int32_t *d_slot_mapping, int32_t num_tokens, int32_t num_pages, int32_t page_size,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void *stream);
+
+/* ------------------------------------------------------------------------------------------ cb_paged_attention */
+
+typedef struct cb_attn_args {
+    void *out;                    /* device [T][Hq][D], written for every token of the plan                       */
+    const void *q;                /* device [T][Hq][D]                                                           */
+    const void *k_cache;          /* device, layout above                                                        */
+    const void *v_cache;          /* device, layout above                                                        */
+    const int32_t *block_table;   /* device [N][table_width]: physical page per logical block (or ring slot)     */
+    const int32_t *plan;          /* device copy of the int32 plan written by cb_plan_attention                 */
+    cb_plan plan_info;            /* host copy of that plan's header                                             */
+    cb_attn_shape shape;          /* the shape the plan was made for                                             */
+    int32_t num_pages;            /* pages in each cache tensor                                                  */
+    int32_t table_width;          /* row stride of block_table                                                   */
+    float scale;                  /* softmax scale applied to q.k                                                */
+    void *workspace;              /* device scratch of cb_paged_attention_workspace_size() bytes (256-aligned)  */
+    size_t workspace_bytes;
+    int32_t phases;               /* 0 = the whole step; else a mask of CB_PHASE_* launching only those kernels,
+                                     in the fixed order (lets a caller bracket one kernel with events)           */
+} cb_attn_args;
+
+#define CB_PHASE_DECODE 1         /* split-KV decode kernel                                                     */
+#define CB_PHASE_ROWWISE 2        /* general per-token kernel                                                   */
+#define CB_PHASE_PREFILL 4        /* prefill-tile kernel                                                        */
+#define CB_PHASE_COMBINE 8        /* merge of split rows; needs the phases that wrote its partials to have run  */
+
+/* Bytes of device workspace cb_paged_attention needs for this plan (0 if none). */
+size_t cb_paged_attention_workspace_size(const cb_attn_args *args);
+
+/*
+ * Attention of every token of the plan ("Continuous Batching" blog, sections "优化：偏移实现 Mask" and "扩展：vLLM
+ * v1 中的实现": per request, keys 0..context_len+local_q through block_table; no mask is materialised).
+ * Launches, in order on `stream`: the split-KV decode kernel, the general per-token kernel, the prefill-tile kernel,
+ * then the merge of split rows. Reads the caches only. Page ids read from block_table are clamped into
+ * [0, num_pages) so a corrupt table cannot fault the device (results are then meaningless).
+ * Returns CB_OK, CB_E_INVAL, CB_E_UNSUPPORTED, CB_E_WORKSPACE or CB_E_HIP.
+ */
+cb_status cb_paged_attention(const cb_attn_args *args, void *stream);
+
+/* --------------------------------------------------------------------------------------------------- utilities */
+
+const char *cb_status_str(cb_status status);
+int32_t cb_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CB_H */

@@ -108,17 +108,20 @@ def pages_reference(w, layer: int, sched, pages=None):
             k[n, off] = kr
             v[n, off] = vr
 
-    # history of every admitted request (scheduled or not), in position order
+    # history of every admitted request (scheduled or not): walk its logical blocks, keep those whose physical page
+    # was asked for, and write their positions in order
     for i, rq in enumerate(w.requests):
         if len(rq.pages[layer]) == 0 or rq.num_computed == 0:
             continue
         a, b = history_range(w, layer, rq.num_computed)
-        if b <= a:
-            continue
-        kh = w.values("k", i, layer, a, b)
-        vh = w.values("v", i, layer, a, b)
-        for n, pos in enumerate(range(a, b)):
-            put(A.slot_of(rq.pages[layer], pos, P, lay.ring_len), kh[n], vh[n])
+        for blk in range(a // P, (b - 1) // P + 1 if b > a else a // P):
+            if A.physical_page(rq.pages[layer], blk, lay.ring_len) not in where:
+                continue
+            s, e = max(a, blk * P), min(b, (blk + 1) * P)
+            kh = w.values("k", i, layer, s, e)
+            vh = w.values("v", i, layer, s, e)
+            for n, pos in enumerate(range(s, e)):
+                put(A.slot_of(rq.pages[layer], pos, P, lay.ring_len), kh[n], vh[n])
     # the step's append
     _, kn, vn = step_inputs(w, layer, sched)
     for t, slot in enumerate(sched["layers"][layer]["slot_mapping"]):

@@ -1,0 +1,240 @@
+"""MI355X-native mixed-batch paged attention step of continuous batching.
+
+Thin Python binding over the C ABI of libcb.so (include/cb.h); same call names. It only marshals arguments: the
+scheduler, the planner and every kernel run inside the library. Device buffers are torch tensors (torch is used for
+device memory and streams only). There is no fallback: if libcb.so is missing or the GPU is absent, calls raise.
+
+    build_metadata   -> cb_build_metadata   (host)
+    plan_attention   -> cb_plan_attention   (host)
+    kv_append        -> cb_kv_append        (device, current torch stream)
+    paged_attention  -> cb_paged_attention  (device, current torch stream)
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import _abi
+from ._abi import (CB_DECODING, CB_DTYPE_BF16, CB_DTYPE_F32, CB_E_CAPACITY, CB_E_NOSPACE, CB_OK,  # noqa: F401
+                   CB_PHASE_COMBINE, CB_PHASE_DECODE, CB_PHASE_PREFILL, CB_PHASE_ROWWISE, CB_PREFILLING, CB_WAITING,
+                   CbError)
+
+__all__ = ["build_metadata", "plan_attention", "kv_append", "paged_attention", "workspace_size", "AttnPlan",
+           "load_library", "CbError"]
+
+
+def load_library():
+    return _abi.load()
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_abi.i32p) if a.size else C.cast(C.c_void_p(0), _abi.i32p)
+
+
+# ------------------------------------------------------------------------------------------- cb_build_metadata
+
+def build_metadata(requests, layers, max_batch_tokens: int, max_requests: int, page_size: int,
+                   safety_margin: float = 0.0, pad_page: int = 0) -> dict:
+    """Schedule one step (cb_build_metadata).
+
+    requests: sequence of objects with .id, .state (0 decoding / 1 prefilling / 2 waiting), .num_computed,
+      .num_pending and .pages (one int array per layer), in arrival order.
+    layers: sequence of dicts {ring_len, window_left, pool_pages, free_pages}.
+    Returns a dict with "status" (int) and, unless the input was invalid, the metadata as numpy arrays.
+    """
+    lib = _abi.load()
+    n = len(requests)
+    L = len(layers)
+    keep = []
+    reqs = (_abi.cb_req * max(n, 1))()
+    for i, rq in enumerate(requests):
+        reqs[i].id = int(rq.id)
+        reqs[i].state = int(rq.state)
+        reqs[i].num_computed = int(rq.num_computed)
+        reqs[i].num_pending = int(rq.num_pending)
+        for l in range(L):
+            p = _i32(rq.pages[l])
+            keep.append(p)
+            reqs[i].n_pages[l] = p.size
+            reqs[i].pages[l] = _ptr(p)
+    pools = (_abi.cb_layer_pool * max(L, 1))()
+    for l, lay in enumerate(layers):
+        f = _i32(lay["free_pages"])
+        keep.append(f)
+        pools[l].ring_len = int(lay["ring_len"])
+        pools[l].window_left = int(lay["window_left"])
+        pools[l].pool_pages = int(lay["pool_pages"])
+        pools[l].n_free = f.size
+        pools[l].free_pages = _ptr(f)
+    params = _abi.cb_sched_params(int(max_batch_tokens), int(max_requests), int(page_size), int(pad_page), L,
+                                  float(safety_margin))
+    step = _abi.cb_step()
+    cap = 4096
+    while True:
+        buf = np.zeros(cap, dtype=np.int32)
+        st = lib.cb_build_metadata(reqs, n, C.byref(params), pools, _ptr(buf), cap, C.byref(step))
+        if st != CB_E_CAPACITY:
+            break
+        cap = int(step.used)
+    if st not in (CB_OK, CB_E_NOSPACE):
+        return {"status": st}
+    N, T = step.num_reqs, step.num_tokens
+    o = {"status": st, "num_reqs": N, "num_tokens": T, "num_decodes": step.num_decodes,
+         "max_q_len": step.max_q_len, "max_seq_len": step.max_seq_len,
+         "query_start_loc": buf[step.off_query_start_loc:step.off_query_start_loc + N + 1].copy(),
+         "seq_lens": buf[step.off_seq_lens:step.off_seq_lens + N].copy(),
+         "req_index": buf[step.off_req_index:step.off_req_index + N].copy(),
+         "stalled": buf[step.off_stalled:step.off_stalled + step.n_stalled].copy(),
+         "first_rejected": step.first_rejected, "held_by_margin": bool(step.held_by_margin), "layers": []}
+    for l in range(L):
+        w = step.table_width[l]
+        bt = buf[step.off_block_table[l]:step.off_block_table[l] + N * w].reshape(N, w).copy()
+        o["layers"].append({"block_table": bt,
+                            "slot_mapping": buf[step.off_slot_mapping[l]:step.off_slot_mapping[l] + T].copy(),
+                            "ring_len": buf[step.off_ring_len[l]:step.off_ring_len[l] + N].copy(),
+                            "used_pages": step.used_pages[l], "width": w})
+    return o
+
+
+# ------------------------------------------------------------------------------------------- cb_plan_attention
+
+@dataclass
+class AttnPlan:
+    info: _abi.cb_plan
+    shape: _abi.cb_attn_shape
+    buffer: np.ndarray          # host int32 plan
+
+    def counts(self) -> dict:
+        i = self.info
+        return {"decode": i.n_decode, "prefill": i.n_prefill, "rowwise": i.n_rowwise, "combine": i.n_combine,
+                "partials": i.n_partials, "decode_split": i.decode_split, "prefill_split": i.prefill_split,
+                "prefill_tokens": i.prefill_tokens}
+
+    def items(self, kind: str) -> np.ndarray:
+        i = self.info
+        n, off, w = {"decode": (i.n_decode, i.off_decode, 8), "prefill": (i.n_prefill, i.off_prefill, 8),
+                     "rowwise": (i.n_rowwise, i.off_rowwise, 8), "combine": (i.n_combine, i.off_combine, 4)}[kind]
+        return self.buffer[off:off + n * w].reshape(n, w)
+
+
+def _dtype_code(dtype) -> int:
+    import torch
+    if dtype in (torch.float32, "f32", "float32"):
+        return CB_DTYPE_F32
+    if dtype in (torch.bfloat16, "bf16", "bfloat16"):
+        return CB_DTYPE_BF16
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+def plan_attention(query_start_loc, seq_lens, ring_len, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                   page_size: int, dtype, window_left: int = -1, decode_split: int = 0,
+                   prefill_split: int = 0) -> AttnPlan:
+    """Split a step into kernel work items (cb_plan_attention). ring_len: per-row ring lengths or None."""
+    lib = _abi.load()
+    qsl = _i32(query_start_loc)
+    seq = _i32(seq_lens)
+    n = seq.size
+    rl = None if ring_len is None else _i32(ring_len)
+    shape = _abi.cb_attn_shape(int(num_q_heads), int(num_kv_heads), int(head_dim), int(page_size),
+                               _dtype_code(dtype), int(window_left), int(decode_split), int(prefill_split))
+    info = _abi.cb_plan()
+    cap = 1024
+    while True:
+        buf = np.zeros(cap, dtype=np.int32)
+        st = lib.cb_plan_attention(_ptr(qsl), _ptr(seq), None if rl is None else _ptr(rl), n, C.byref(shape),
+                                   _ptr(buf), cap, C.byref(info))
+        if st != CB_E_CAPACITY:
+            break
+        cap = int(info.used)
+    if st != CB_OK:
+        raise CbError(st, "cb_plan_attention")
+    return AttnPlan(info, shape, buf[:int(info.used)].copy())
+
+
+# ------------------------------------------------------------------------------------------------ device calls
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return C.c_void_p(getattr(stream, "cuda_stream", stream))
+
+
+def _check_dev(t, name):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None) -> None:
+    """cb_kv_append: k_cache [pages, Hkv, P, D], v_cache [pages, Hkv, D, P], k_new/v_new [T, Hkv, D], slot_mapping
+    [T] int32 (device tensors)."""
+    lib = _abi.load()
+    for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache"), (k_new, "k_new"), (v_new, "v_new"),
+                  (slot_mapping, "slot_mapping")):
+        _check_dev(t, nm)
+    n_pages, Hkv, P, D = k_cache.shape
+    if tuple(v_cache.shape) != (n_pages, Hkv, D, P) or k_new.shape[1:] != (Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("cache / new-row shapes do not match")
+    if slot_mapping.numel() != k_new.shape[0] or str(slot_mapping.dtype) != "torch.int32":
+        raise ValueError("slot_mapping must be int32 [T]")
+    if not (k_cache.dtype == v_cache.dtype == k_new.dtype == v_new.dtype):
+        raise ValueError("dtype mismatch")
+    st = lib.cb_kv_append(k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                          slot_mapping.data_ptr(), k_new.shape[0], n_pages, P, Hkv, D, _dtype_code(k_cache.dtype),
+                          _stream(stream))
+    if st != CB_OK:
+        raise CbError(st, "cb_kv_append")
+
+
+def _args(out, q, k_cache, v_cache, block_table, plan: AttnPlan, plan_dev, scale, workspace, phases=0):
+    a = _abi.cb_attn_args()
+    a.out, a.q = out.data_ptr(), q.data_ptr()
+    a.k_cache, a.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+    a.block_table = block_table.data_ptr()
+    a.plan = plan_dev.data_ptr()
+    a.plan_info = plan.info
+    a.shape = plan.shape
+    a.num_pages = k_cache.shape[0]
+    a.table_width = block_table.shape[1] if block_table.dim() == 2 else 0
+    a.scale = float(scale)
+    a.workspace = workspace.data_ptr() if workspace is not None else None
+    a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    a.phases = int(phases)
+    return a
+
+
+def workspace_size(plan: AttnPlan) -> int:
+    a = _abi.cb_attn_args()
+    a.plan_info = plan.info
+    a.shape = plan.shape
+    return int(_abi.load().cb_paged_attention_workspace_size(C.byref(a)))
+
+
+def paged_attention(out, q, k_cache, v_cache, block_table, plan: AttnPlan, plan_dev, scale: float,
+                    workspace=None, stream=None, phases: int = 0) -> None:
+    """cb_paged_attention: out/q [T, Hq, D]; caches as in kv_append; block_table [N, width] int32; plan_dev = the
+    plan's int32 buffer on the device; workspace: a device byte tensor of at least workspace_size(plan) bytes;
+    phases: 0 for the whole step, or a mask of CB_PHASE_* to launch only some of its kernels."""
+    lib = _abi.load()
+    for t, nm in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                  (block_table, "block_table"), (plan_dev, "plan")):
+        _check_dev(t, nm)
+    sh = plan.shape
+    if tuple(q.shape) != (plan.info.num_tokens, sh.num_q_heads, sh.head_dim) or out.shape != q.shape:
+        raise ValueError("q/out shape does not match the plan")
+    if tuple(k_cache.shape[1:]) != (sh.num_kv_heads, sh.page_size, sh.head_dim):
+        raise ValueError("k_cache shape does not match the plan")
+    if tuple(v_cache.shape) != (k_cache.shape[0], sh.num_kv_heads, sh.head_dim, sh.page_size):
+        raise ValueError("v_cache shape does not match the plan")
+    if plan_dev.numel() < plan.buffer.size or str(plan_dev.dtype) != "torch.int32":
+        raise ValueError("plan_dev must hold the plan's int32 buffer")
+    a = _args(out, q, k_cache, v_cache, block_table, plan, plan_dev, scale, workspace, phases)
+    st = lib.cb_paged_attention(C.byref(a), _stream(stream))
+    if st != CB_OK:
+        raise CbError(st, "cb_paged_attention")

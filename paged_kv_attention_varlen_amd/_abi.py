@@ -1,0 +1,110 @@
+"""ctypes mirror of include/cb.h and the loader of the in-tree libcb.so."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcb.so")
+
+CB_OK, CB_E_INVAL, CB_E_NOSPACE, CB_E_CAPACITY, CB_E_UNSUPPORTED, CB_E_WORKSPACE, CB_E_HIP = range(7)
+CB_DTYPE_F32, CB_DTYPE_BF16 = 0, 1
+CB_DECODING, CB_PREFILLING, CB_WAITING = 0, 1, 2
+CB_MAX_LAYERS = 2
+CB_PHASE_DECODE, CB_PHASE_ROWWISE, CB_PHASE_PREFILL, CB_PHASE_COMBINE = 1, 2, 4, 8
+ABI_VERSION = 1
+
+i32p = C.POINTER(C.c_int32)
+
+
+class cb_req(C.Structure):
+    _fields_ = [("id", C.c_int64), ("state", C.c_int32), ("num_computed", C.c_int32), ("num_pending", C.c_int32),
+                ("n_pages", C.c_int32 * CB_MAX_LAYERS), ("pages", i32p * CB_MAX_LAYERS)]
+
+
+class cb_layer_pool(C.Structure):
+    _fields_ = [("ring_len", C.c_int32), ("window_left", C.c_int32), ("pool_pages", C.c_int32),
+                ("n_free", C.c_int32), ("free_pages", i32p)]
+
+
+class cb_sched_params(C.Structure):
+    _fields_ = [("max_batch_tokens", C.c_int32), ("max_requests", C.c_int32), ("page_size", C.c_int32),
+                ("pad_page", C.c_int32), ("n_layers", C.c_int32), ("safety_margin", C.c_float)]
+
+
+class cb_step(C.Structure):
+    _fields_ = [("num_reqs", C.c_int32), ("num_tokens", C.c_int32), ("num_decodes", C.c_int32),
+                ("max_q_len", C.c_int32), ("max_seq_len", C.c_int32), ("n_stalled", C.c_int32),
+                ("first_rejected", C.c_int32), ("held_by_margin", C.c_int32),
+                ("used_pages", C.c_int32 * CB_MAX_LAYERS), ("table_width", C.c_int32 * CB_MAX_LAYERS),
+                ("off_query_start_loc", C.c_int64), ("off_seq_lens", C.c_int64), ("off_req_index", C.c_int64),
+                ("off_stalled", C.c_int64), ("off_block_table", C.c_int64 * CB_MAX_LAYERS),
+                ("off_slot_mapping", C.c_int64 * CB_MAX_LAYERS), ("off_ring_len", C.c_int64 * CB_MAX_LAYERS),
+                ("used", C.c_int64)]
+
+
+class cb_attn_shape(C.Structure):
+    _fields_ = [("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("page_size", C.c_int32), ("dtype", C.c_int32), ("window_left", C.c_int32),
+                ("decode_split", C.c_int32), ("prefill_split", C.c_int32)]
+
+
+class cb_plan(C.Structure):
+    _fields_ = [("n_decode", C.c_int32), ("n_prefill", C.c_int32), ("n_rowwise", C.c_int32),
+                ("n_combine", C.c_int32), ("n_partials", C.c_int32), ("decode_split", C.c_int32),
+                ("prefill_split", C.c_int32), ("prefill_tokens", C.c_int32), ("num_tokens", C.c_int32),
+                ("max_page_index", C.c_int32), ("off_decode", C.c_int64), ("off_prefill", C.c_int64),
+                ("off_rowwise", C.c_int64), ("off_combine", C.c_int64), ("used", C.c_int64)]
+
+
+class cb_attn_args(C.Structure):
+    _fields_ = [("out", C.c_void_p), ("q", C.c_void_p), ("k_cache", C.c_void_p), ("v_cache", C.c_void_p),
+                ("block_table", C.c_void_p), ("plan", C.c_void_p), ("plan_info", cb_plan),
+                ("shape", cb_attn_shape), ("num_pages", C.c_int32), ("table_width", C.c_int32),
+                ("scale", C.c_float), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+                ("phases", C.c_int32)]
+
+
+EXPORTS = ("cb_build_metadata", "cb_plan_attention", "cb_kv_append", "cb_paged_attention",
+           "cb_paged_attention_workspace_size", "cb_status_str", "cb_abi_version")
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libcb.so (built in-tree by `python -m paged_kv_attention_varlen_amd.build`). Raises if it is missing:
+    there is no fallback implementation."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m paged_kv_attention_varlen_amd.build`")
+    lib = C.CDLL(path)
+    lib.cb_build_metadata.restype = C.c_int32
+    lib.cb_build_metadata.argtypes = [C.POINTER(cb_req), C.c_int32, C.POINTER(cb_sched_params),
+                                      C.POINTER(cb_layer_pool), i32p, C.c_int64, C.POINTER(cb_step)]
+    lib.cb_plan_attention.restype = C.c_int32
+    lib.cb_plan_attention.argtypes = [i32p, i32p, i32p, C.c_int32, C.POINTER(cb_attn_shape), i32p, C.c_int64,
+                                      C.POINTER(cb_plan)]
+    lib.cb_kv_append.restype = C.c_int32
+    lib.cb_kv_append.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                                 C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
+    lib.cb_paged_attention.restype = C.c_int32
+    lib.cb_paged_attention.argtypes = [C.POINTER(cb_attn_args), C.c_void_p]
+    lib.cb_paged_attention_workspace_size.restype = C.c_size_t
+    lib.cb_paged_attention_workspace_size.argtypes = [C.POINTER(cb_attn_args)]
+    lib.cb_status_str.restype = C.c_char_p
+    lib.cb_status_str.argtypes = [C.c_int32]
+    lib.cb_abi_version.restype = C.c_int32
+    lib.cb_abi_version.argtypes = []
+    if lib.cb_abi_version() != ABI_VERSION:
+        raise ImportError(f"libcb.so ABI version {lib.cb_abi_version()} != binding version {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+class CbError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = load().cb_status_str(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{what}: {msg} (status {status})")

@@ -1,0 +1,756 @@
+// Device half of the cb library for gfx950 (MI355X): KV append, split-KV decode, per-token general kernel,
+// prefill tiles, and the merge of split rows. All kernels read their work from the host-built plan.
+//
+// Layouts (see include/cb.h):
+//   k_cache [page][kv_head][offset][d]    -- a key row is D contiguous elements
+//   v_cache [page][kv_head][d][offset]    -- a value column over the page's offsets is contiguous
+// so both contractions (q.k over d, p.v over keys) read their reduction index contiguously per lane, which is what
+// the MFMA operand layouts want: 8 consecutive bf16 of the reduction dimension per lane.
+//
+// Softmax runs in the log2 domain: scores are multiplied by scale*log2(e) once and exponentiated with exp2;
+// partial results store the running maximum in those units.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "cb.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kNegInf = -INFINITY;
+
+__device__ __forceinline__ u32x4 load16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void store16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// Physical page of a logical block of one request (ring slot in ring mode), clamped into the pool so that a
+// corrupt table cannot send a load outside the cache tensors.
+__device__ __forceinline__ int lookup_page(const int32_t *bt_row, int logical, int ring, int num_pages) {
+    const int idx = ring > 0 ? logical % ring : logical;
+    const int p = bt_row[idx];
+    return p < 0 ? 0 : (p >= num_pages ? num_pages - 1 : p);
+}
+
+// Zero the bf16 elements of an 8-wide group whose key (key0 + e) lies outside [lo, hi).
+__device__ __forceinline__ u32x4 mask_keys8(u32x4 v, int key0, int lo, int hi) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int k = key0 + 2 * w;
+        uint32_t m = 0;
+        if (k >= lo && k < hi) m |= 0x0000FFFFu;
+        if (k + 1 >= lo && k + 1 < hi) m |= 0xFFFF0000u;
+        v[w] &= m;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) x += __shfl_xor(x, s);
+    return x;
+}
+
+// ============================================================================================== KV append
+//
+// One thread per (token, kv head, 16-byte chunk of the row). K chunks are copied whole; the matching V elements
+// are scattered into their d-rows at the token's page offset.
+
+template <typename T>
+__global__ __launch_bounds__(256) void kv_append_kernel(T *__restrict__ kc, T *__restrict__ vc,
+                                                        const T *__restrict__ kn, const T *__restrict__ vn,
+                                                        const int32_t *__restrict__ slots, int num_tokens,
+                                                        int num_pages, int P, int Hkv, int D) {
+    constexpr int E = 16 / sizeof(T);
+    const int chunks = D / E;
+    const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (gid >= int64_t(num_tokens) * Hkv * chunks) return;
+    const int c = int(gid % chunks);
+    const int64_t rest = gid / chunks;
+    const int g = int(rest % Hkv);
+    const int64_t t = rest / Hkv;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= int64_t(num_pages) * P) return;
+    const int64_t page = slot / P;
+    const int off = int(slot % P);
+    const int64_t src = (t * Hkv + g) * D + int64_t(c) * E;
+    store16(kc + ((page * Hkv + g) * P + off) * D + int64_t(c) * E, load16(kn + src));
+    const u32x4 v = load16(vn + src);
+    const T *ve = reinterpret_cast<const T *>(&v);
+    T *vrow = vc + ((page * Hkv + g) * D + int64_t(c) * E) * P + off;
+#pragma unroll
+    for (int e = 0; e < E; ++e) vrow[int64_t(e) * P] = ve[e];
+}
+
+// ===================================================================== split-KV decode (bf16, MFMA 16x16x32)
+//
+// Work group = one (decode row split, kv head); 4 waves take the split's 32-key tiles round-robin and merge their
+// online-softmax states through LDS at the end. All G query heads of the kv head ride in the N dimension of the
+// MFMAs (padded to 16), so each K/V byte is read once for the whole group.
+//
+// Per 32-key tile and wave:
+//   scores  S[key][head] = K[key][:] . Q[head][:]      2 x D/32 MFMAs; A = K rows, B = Q^T
+//   output  O[d][head]  += V^T[d][key] . P[key][head]  D/16 MFMAs;     A = V^T (d-major page), B = P^T
+// MFMA 16x16x32 bf16 operands: lane l holds A[l%16][8(l/16) .. +8] and B[8(l/16) .. +8][l%16]; the result gives
+// lane l the entries [4(l/16) .. +4][l%16]. The key order inside the tile is permuted so that after the QK product
+// lane l owns the scores of keys 8(l/16) .. 8(l/16)+7 for head l%16 -- exactly its B operand of the PV product --
+// and a V^T operand of 8 consecutive keys is one 16-byte load.
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_kernel(const uint16_t *__restrict__ q, uint16_t *__restrict__ out,
+                                                     const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
+                                                     const int32_t *__restrict__ block_table, int table_width,
+                                                     int num_pages, const int32_t *__restrict__ items,
+                                                     float *__restrict__ part_o, float *__restrict__ part_ml, int Hq,
+                                                     int Hkv, int P_log2, float scale_log2e) {
+    constexpr int KB = D / 32;   // QK MFMAs per 16-key half tile
+    constexpr int DB = D / 16;   // PV MFMAs (16 d-rows each)
+    __shared__ float sm_o[4][D][17];
+    __shared__ float sm_m[4][16];
+    __shared__ float sm_l[4][16];
+
+    const int32_t *it = items + int64_t(blockIdx.x) * 8;
+    const int r = it[0], t = it[1], kv_lo = it[3], kv_hi = it[4], slot = it[5], ring = it[6];
+    const int g = blockIdx.y;
+    const int G = Hq / Hkv;
+    const int P = 1 << P_log2;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15;   // head in the group (N index) and A row index
+    const int rg = lane >> 4;    // 0..3
+    const int32_t *bt = block_table + int64_t(r) * table_width;
+
+    // Q as the B operand of the QK product: head `col`, d = 32kb + 8rg .. +8
+    bf16x8 qf[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        u32x4 v = {0, 0, 0, 0};
+        if (col < G) v = load16(q + (int64_t(t) * Hq + g * G + col) * D + 32 * kb + 8 * rg);
+        qf[kb] = as_bf16x8(v);
+    }
+
+    // K row handled by this lane in each half tile: A row `col` of half hf holds key 8(col/4) + 4hf + col%4
+    const int krow0 = 8 * (col >> 2) + (col & 3);
+
+    float m = kNegInf, l = 0.f;
+    f32x4 acc[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int tile_first = kv_lo >> 5, tile_last = (kv_hi - 1) >> 5;
+    for (int tile = tile_first + wave; tile <= tile_last; tile += 4) {
+        const int base = tile << 5;
+        const bool edge = base < kv_lo || base + 32 > kv_hi;
+        // ---- loads: K rows for both halves, V^T columns of keys base+8rg .. +8
+        u32x4 kreg[2][KB];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int key = base + krow0 + 4 * hf;
+            if (key >= kv_lo && key < kv_hi) {
+                const int page = lookup_page(bt, key >> P_log2, ring, num_pages);
+                const uint16_t *src = kc + ((int64_t(page) * Hkv + g) * P + (key & (P - 1))) * D + 8 * rg;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) kreg[hf][kb] = load16(src + 32 * kb);
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) kreg[hf][kb] = u32x4{0, 0, 0, 0};
+            }
+        }
+        u32x4 vreg[DB];
+        const int key8 = base + 8 * rg;
+        if (key8 + 8 > kv_lo && key8 < kv_hi) {
+            const int first = key8 < kv_lo ? kv_lo : key8;   // any valid key of the group locates the page
+            const int page = lookup_page(bt, first >> P_log2, ring, num_pages);
+            const uint16_t *src = vc + ((int64_t(page) * Hkv + g) * D + col) * P + (key8 & (P - 1));
+#pragma unroll
+            for (int b = 0; b < DB; ++b) vreg[b] = load16(src + int64_t(16 * b) * P);
+            if (edge) {
+#pragma unroll
+                for (int b = 0; b < DB; ++b) vreg[b] = mask_keys8(vreg[b], key8, kv_lo, kv_hi);
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < DB; ++b) vreg[b] = u32x4{0, 0, 0, 0};
+        }
+        // ---- scores
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[0][kb]), qf[kb], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[1][kb]), qf[kb], s1, 0, 0, 0);
+        }
+        float s[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            s[u] = s0[u] * scale_log2e;
+            s[4 + u] = s1[u] * scale_log2e;
+        }
+        if (edge) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int key = key8 + e;
+                if (key < kv_lo || key >= kv_hi) s[e] = kNegInf;
+            }
+        }
+        // ---- online softmax for head `col` (its 32 keys sit in lanes col, col+16, col+32, col+48)
+        float tmax = s[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, s[e]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m, tmax);
+        const float m_use = m_new == kNegInf ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+        bf16x8 pf;
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(s[e] - m_use);
+            psum += p;
+            pf[e] = static_cast<__bf16>(p);
+        }
+        l = l * alpha + psum;
+        m = m_new;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+            acc[b] *= alpha;
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vreg[b]), pf, acc[b], 0, 0, 0);
+        }
+    }
+    // ---- per-wave totals, then merge the 4 waves
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (rg == 0) {
+        sm_m[wave][col] = m;
+        sm_l[wave][col] = l;
+    }
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sm_o[wave][16 * b + 4 * rg + u][col] = acc[b][u];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+        const int n = idx / D, d = idx % D;
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][n]);
+        float L = 0.f, O = 0.f;
+        if (M != kNegInf) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float f = __builtin_amdgcn_exp2f(sm_m[w][n] - M);
+                L += sm_l[w][n] * f;
+                O += sm_o[w][d][n] * f;
+            }
+        }
+        const int h = g * G + n;
+        if (slot < 0) {
+            out[(int64_t(t) * Hq + h) * D + d] = f32_to_bf16(L > 0.f ? O / L : 0.f);
+        } else {
+            part_o[(int64_t(slot) * Hq + h) * D + d] = O;
+            if (d == 0) {
+                part_ml[(int64_t(slot) * Hq + h) * 2 + 0] = M;
+                part_ml[(int64_t(slot) * Hq + h) * 2 + 1] = L;
+            }
+        }
+    }
+}
+
+// ========================================================================= general per-token kernel (VALU)
+//
+// One wave per (token split, kv head, group of up to 16 query heads). Used for fp32 and for shapes the MFMA
+// kernels do not cover. Keys are taken 64 at a time, one per lane: each lane computes its key's scores for all the
+// group's heads; the wave then folds the chunk into the running softmax, and the lanes switch to one d each for
+// the weighted sum of V.
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x);
+template <>
+__device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) { return f32_to_bf16(x); }
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void rowwise_kernel(const T *__restrict__ q, T *__restrict__ out,
+                                                     const T *__restrict__ kc, const T *__restrict__ vc,
+                                                     const int32_t *__restrict__ block_table, int table_width,
+                                                     int num_pages, const int32_t *__restrict__ items,
+                                                     float *__restrict__ part_o, float *__restrict__ part_ml, int Hq,
+                                                     int Hkv, int P_log2, float scale_log2e) {
+    constexpr int HG = 16;        // query heads per wave
+    constexpr int DPL = D / 64;   // d values per lane in the V sum
+    __shared__ float sq[HG][D];
+    __shared__ float sp[HG][64];
+
+    const int32_t *it = items + int64_t(blockIdx.x) * 8;
+    const int r = it[0], t = it[1], kv_lo = it[3], kv_hi = it[4], slot = it[5], ring = it[6];
+    const int g = blockIdx.y;
+    const int G = Hq / Hkv;
+    const int h0 = blockIdx.z * HG;
+    const int nh = min(HG, G - h0);
+    const int P = 1 << P_log2;
+    const int lane = threadIdx.x;
+    const int32_t *bt = block_table + int64_t(r) * table_width;
+
+    for (int idx = lane; idx < HG * D; idx += 64) {
+        const int n = idx / D, d = idx % D;
+        sq[n][d] = n < nh ? to_f32(q[(int64_t(t) * Hq + g * G + h0 + n) * D + d]) : 0.f;
+    }
+    __syncthreads();
+
+    float m[HG], l[HG], acc[HG][DPL];
+#pragma unroll
+    for (int n = 0; n < HG; ++n) {
+        m[n] = kNegInf;
+        l[n] = 0.f;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) acc[n][j] = 0.f;
+    }
+
+    for (int base = kv_lo; base < kv_hi; base += 64) {
+        const int key = base + lane;
+        float s[HG];
+#pragma unroll
+        for (int n = 0; n < HG; ++n) s[n] = 0.f;
+        if (key < kv_hi) {
+            const int page = lookup_page(bt, key >> P_log2, ring, num_pages);
+            const T *krow = kc + ((int64_t(page) * Hkv + g) * P + (key & (P - 1))) * D;
+            for (int d = 0; d < D; ++d) {
+                const float kv = to_f32(krow[d]);
+#pragma unroll
+                for (int n = 0; n < HG; ++n) s[n] = fmaf(sq[n][d], kv, s[n]);
+            }
+        }
+        const int nkeys = min(64, kv_hi - base);
+#pragma unroll
+        for (int n = 0; n < HG; ++n) {
+            const float sc = key < kv_hi ? s[n] * scale_log2e : kNegInf;
+            const float cmax = wave_max(sc);
+            const float m_new = fmaxf(m[n], cmax);
+            const float alpha = exp2f(m[n] - m_new);
+            const float p = exp2f(sc - m_new);
+            l[n] = l[n] * alpha + wave_sum(p);
+            m[n] = m_new;
+            sp[n][lane] = p;
+#pragma unroll
+            for (int j = 0; j < DPL; ++j) acc[n][j] *= alpha;
+        }
+        __syncthreads();
+        for (int j = 0; j < nkeys; ++j) {
+            const int kk = base + j;
+            const int page = lookup_page(bt, kk >> P_log2, ring, num_pages);
+            const T *vcol = vc + (int64_t(page) * Hkv + g) * D * P + (kk & (P - 1));
+#pragma unroll
+            for (int jj = 0; jj < DPL; ++jj) {
+                const float vv = to_f32(vcol[int64_t(lane + 64 * jj) * P]);
+#pragma unroll
+                for (int n = 0; n < HG; ++n) acc[n][jj] = fmaf(sp[n][j], vv, acc[n][jj]);
+            }
+        }
+        __syncthreads();
+    }
+    for (int n = 0; n < nh; ++n) {
+        const int h = g * G + h0 + n;
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) {
+            const int d = lane + 64 * jj;
+            if (slot < 0) {
+                out[(int64_t(t) * Hq + h) * D + d] = from_f32<T>(l[n] > 0.f ? acc[n][jj] / l[n] : 0.f);
+            } else {
+                part_o[(int64_t(slot) * Hq + h) * D + d] = acc[n][jj];
+            }
+        }
+        if (slot >= 0 && lane == 0) {
+            part_ml[(int64_t(slot) * Hq + h) * 2 + 0] = m[n];
+            part_ml[(int64_t(slot) * Hq + h) * 2 + 1] = l[n];
+        }
+    }
+}
+
+// ======================================================================= prefill tiles (bf16, MFMA 32x32x16)
+//
+// Work group = one (tile of query tokens x the G heads of a kv head = 128 rows, KV range, kv head). Rows are
+// token-major (row = token * G + head). Each wave owns 32 rows. For each 64-key tile the whole group stages K rows
+// and V^T columns in LDS (coalesced page reads), then per 32-key half each wave computes
+//   S^T[key][row] = K[key][:] . Q[row][:]         D/16 MFMAs; A = K rows (from LDS), B = Q^T (registers)
+//   O^T[d][row]  += V^T[d][key] . P^T[key][row]   2 x D/32 MFMAs; A = V^T (from LDS), B = P^T (registers)
+// MFMA 32x32x16 bf16 operands: lane l holds A[l%32][8(l/32) .. +8] and B[8(l/32) .. +8][l%32]; the result gives lane l
+// column l%32 and rows 8(v/4) + 4(l/32) + v%4 for v = 0..15. Keys are fed to the QK product in an order with bits 2
+// and 3 of the index swapped, so that lane l's 16 scores are keys 8(l/32) + 16kk + 0..7 (kk = 0, 1): each group of
+// 8 is one B operand of the PV product, and the matching V^T operand is 8 consecutive keys of one d-row.
+
+constexpr int kPfRows = 128;
+constexpr int kPfKeys = 64;
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_kernel(const uint16_t *__restrict__ q, uint16_t *__restrict__ out,
+                                                      const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
+                                                      const int32_t *__restrict__ block_table, int table_width,
+                                                      int num_pages, const int32_t *__restrict__ items,
+                                                      float *__restrict__ part_o, float *__restrict__ part_ml, int Hq,
+                                                      int Hkv, int P_log2, float scale_log2e, int window_left) {
+    constexpr int KB = D / 16;    // QK MFMAs per 32-key half
+    constexpr int DB = D / 32;    // output blocks of 32 d-rows
+    constexpr int KPAD = D + 8;   // LDS row pitch of K (elements)
+    constexpr int VPAD = kPfKeys + 8;
+    __shared__ uint16_t sk[kPfKeys * KPAD];
+    __shared__ uint16_t sv[D * VPAD];
+
+    const int32_t *it = items + int64_t(blockIdx.x) * 8;
+    const int r = it[0], t0 = it[1], pos0 = it[2], qc = it[3], kv_lo = it[4], kv_hi = it[5];
+    const int slot_base = it[6], ring = it[7];
+    const int g = blockIdx.y;
+    const int G = Hq / Hkv;
+    const int P = 1 << P_log2;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c32 = lane & 31, half = lane >> 5;
+    const int32_t *bt = block_table + int64_t(r) * table_width;
+
+    // this lane's row
+    const int row = 32 * wave + c32;
+    const int ti = row / G, hn = row % G;
+    const bool row_ok = ti < qc;
+    const int pos = pos0 + ti;
+    const int rlo = row_ok ? max(kv_lo, window_left < 0 ? 0 : pos - window_left) : 1;
+    const int rhi = row_ok ? min(pos, kv_hi - 1) : 0;   // inclusive
+
+    // keys any row of the group can see
+    const int ulo = max(kv_lo, window_left < 0 ? 0 : pos0 - window_left);
+    const int uhi = min(kv_hi, pos0 + qc);   // exclusive
+    // keys every valid row of this wave sees (no masking needed inside)
+    const int wr0 = 32 * wave, wr1 = min(32 * wave + 31, qc * G - 1);
+    int full_lo = 0x7fffffff, full_hi = -1;
+    if (wr0 <= wr1) {
+        const int pa = pos0 + wr0 / G, pb = pos0 + wr1 / G;
+        full_lo = max(kv_lo, window_left < 0 ? 0 : pb - window_left);
+        full_hi = min(pa, kv_hi - 1);
+    }
+
+    bf16x8 qf[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        u32x4 v = {0, 0, 0, 0};
+        if (row_ok) v = load16(q + (int64_t(t0 + ti) * Hq + g * G + hn) * D + 16 * kb + 8 * half);
+        qf[kb] = as_bf16x8(v);
+    }
+
+    float m = kNegInf, l = 0.f;
+    f32x16 acc[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+
+    const int krow_sw = ((c32 >> 3) & 1) << 2 | ((c32 >> 2) & 1) << 3 | (c32 & ~12);   // bits 2 and 3 swapped
+
+    const int tile_first = ulo / kPfKeys, tile_last = (uhi - 1) / kPfKeys;
+    for (int tile = tile_first; tile <= tile_last; ++tile) {
+        const int base = tile * kPfKeys;
+        __syncthreads();
+        // ---- stage K rows [64][D]: 16-byte chunks, a key row's chunks on consecutive threads
+        for (int c = threadIdx.x; c < kPfKeys * (D / 8); c += 256) {
+            const int kr = c / (D / 8), cc = c % (D / 8);
+            const int key = base + kr;
+            u32x4 v = {0, 0, 0, 0};
+            if (key >= ulo && key < uhi) {
+                const int page = lookup_page(bt, key >> P_log2, ring, num_pages);
+                v = load16(kc + ((int64_t(page) * Hkv + g) * P + (key & (P - 1))) * D + 8 * cc);
+            }
+            store16(&sk[kr * KPAD + 8 * cc], v);
+        }
+        // ---- stage V^T [D][64]: walk each page's d-major slice contiguously
+        {
+            const int run = P < kPfKeys ? P : kPfKeys;   // keys of one page inside the tile
+            const int per_row = run / 8;                  // 16-byte chunks per d-row of one page
+            for (int c = threadIdx.x; c < D * (kPfKeys / 8); c += 256) {
+                const int pi = c / (D * per_row);
+                const int w = c % (D * per_row);
+                const int d = w / per_row, kk = w % per_row;
+                const int kt = pi * run + 8 * kk;   // key offset inside the tile
+                const int key8 = base + kt;
+                u32x4 v = {0, 0, 0, 0};
+                if (key8 + 8 > ulo && key8 < uhi) {
+                    const int first = key8 < ulo ? ulo : key8;
+                    const int page = lookup_page(bt, first >> P_log2, ring, num_pages);
+                    v = load16(vc + ((int64_t(page) * Hkv + g) * D + d) * P + (key8 & (P - 1)));
+                    if (key8 < ulo || key8 + 8 > uhi) v = mask_keys8(v, key8, ulo, uhi);
+                }
+                store16(&sv[d * VPAD + kt], v);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int sbase = base + 32 * sub;
+            if (sbase >= uhi || sbase + 32 <= ulo) continue;
+            // ---- S^T = K Q^T
+            f32x16 s = {};
+            const uint16_t *ka = &sk[(32 * sub + krow_sw) * KPAD + 8 * half];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(load16(ka + 16 * kb)), qf[kb], s, 0, 0, 0);
+            // lane's 16 scores: keys sbase + 8*half + 16*(v/8) + v%8
+            const bool inner = sbase >= full_lo && sbase + 31 <= full_hi;
+            float sc[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                sc[v] = s[v] * scale_log2e;
+                if (!inner) {
+                    const int key = sbase + 8 * half + 16 * (v >> 3) + (v & 7);
+                    if (key < rlo || key > rhi) sc[v] = kNegInf;
+                }
+            }
+            float tmax = sc[0];
+#pragma unroll
+            for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, sc[v]);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float m_new = fmaxf(m, tmax);
+            const float m_use = m_new == kNegInf ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+            bf16x8 pf[2];
+            float psum = 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float p = __builtin_amdgcn_exp2f(sc[v] - m_use);
+                psum += p;
+                pf[v >> 3][v & 7] = static_cast<__bf16>(p);
+            }
+            l = l * alpha + psum;
+            m = m_new;
+            // ---- O^T += V^T P^T
+#pragma unroll
+            for (int b = 0; b < DB; ++b) {
+                acc[b] *= alpha;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const uint16_t *va = &sv[(32 * b + c32) * VPAD + 32 * sub + 16 * kk + 8 * half];
+                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(load16(va)), pf[kk], acc[b], 0, 0, 0);
+                }
+            }
+        }
+    }
+    l += __shfl_xor(l, 32);
+    if (!row_ok) return;
+    const int h = g * G + hn;
+    const int tok = t0 + ti;
+    // lane holds O^T[d][row] for d = 32b + 8(v/4) + 4*half + v%4
+    if (slot_base < 0) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t *orow = out + (int64_t(tok) * Hq + h) * D;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const int d = 32 * b + 8 * v4 + 4 * half;
+                uint32_t lo2 = uint32_t(f32_to_bf16(acc[b][4 * v4 + 0] * inv)) |
+                               uint32_t(f32_to_bf16(acc[b][4 * v4 + 1] * inv)) << 16;
+                uint32_t hi2 = uint32_t(f32_to_bf16(acc[b][4 * v4 + 2] * inv)) |
+                               uint32_t(f32_to_bf16(acc[b][4 * v4 + 3] * inv)) << 16;
+                *reinterpret_cast<uint2 *>(orow + d) = make_uint2(lo2, hi2);
+            }
+    } else {
+        const int64_t sl = int64_t(slot_base) + ti;
+        float *po = part_o + (sl * Hq + h) * D;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const int d = 32 * b + 8 * v4 + 4 * half;
+                *reinterpret_cast<f32x4 *>(po + d) =
+                    f32x4{acc[b][4 * v4 + 0], acc[b][4 * v4 + 1], acc[b][4 * v4 + 2], acc[b][4 * v4 + 3]};
+            }
+        if (half == 0) {
+            part_ml[(sl * Hq + h) * 2 + 0] = m;
+            part_ml[(sl * Hq + h) * 2 + 1] = l;
+        }
+    }
+}
+
+// =========================================================================================== merge of splits
+//
+// out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s, for each (token, head).
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(T *__restrict__ out, const float *__restrict__ part_o,
+                                                      const float *__restrict__ part_ml,
+                                                      const int32_t *__restrict__ items, int Hq, int D) {
+    const int32_t *it = items + int64_t(blockIdx.x) * 4;
+    const int t = it[0], first = it[1], n = it[2], stride = it[3];
+    for (int idx = threadIdx.x; idx < Hq * D; idx += blockDim.x) {
+        const int h = idx / D, d = idx % D;
+        float M = kNegInf;
+        for (int s = 0; s < n; ++s) M = fmaxf(M, part_ml[((int64_t(first) + int64_t(s) * stride) * Hq + h) * 2]);
+        float L = 0.f, O = 0.f;
+        if (M != kNegInf) {
+            for (int s = 0; s < n; ++s) {
+                const int64_t sl = int64_t(first) + int64_t(s) * stride;
+                const float f = exp2f(part_ml[(sl * Hq + h) * 2] - M);
+                L += part_ml[(sl * Hq + h) * 2 + 1] * f;
+                O += part_o[(sl * Hq + h) * D + d] * f;
+            }
+        }
+        out[(int64_t(t) * Hq + h) * D + d] = from_f32<T>(L > 0.f ? O / L : 0.f);
+    }
+}
+
+inline int ilog2(int x) {
+    int s = 0;
+    while ((1 << s) < x) ++s;
+    return s;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool shape_ok(const cb_attn_shape &s) {
+    return s.num_q_heads > 0 && s.num_kv_heads > 0 && s.num_q_heads % s.num_kv_heads == 0 &&
+           (s.head_dim == 64 || s.head_dim == 128) && s.page_size >= 1 && s.page_size <= 256 &&
+           (s.page_size & (s.page_size - 1)) == 0 && (s.dtype == CB_DTYPE_F32 || s.dtype == CB_DTYPE_BF16) &&
+           s.window_left >= -1;
+}
+
+}  // namespace
+
+// ================================================================================================== C ABI
+
+extern "C" cb_status cb_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                                  const int32_t *d_slot_mapping, int32_t num_tokens, int32_t num_pages,
+                                  int32_t page_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                  void *stream) {
+    if (num_tokens < 0 || num_pages < 1 || page_size < 1 || num_kv_heads < 1 || head_dim < 1) return CB_E_INVAL;
+    if (dtype != CB_DTYPE_F32 && dtype != CB_DTYPE_BF16) return CB_E_UNSUPPORTED;
+    const int esz = dtype == CB_DTYPE_F32 ? 4 : 2;
+    if ((head_dim * esz) % 16 != 0) return CB_E_UNSUPPORTED;
+    if (num_tokens == 0) return CB_OK;
+    if (!k_cache || !v_cache || !k_new || !v_new || !d_slot_mapping) return CB_E_INVAL;
+    const int64_t threads = int64_t(num_tokens) * num_kv_heads * (head_dim * esz / 16);
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > INT32_MAX) return CB_E_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == CB_DTYPE_F32) {
+        hipLaunchKernelGGL(kv_append_kernel<float>, dim3(unsigned(blocks)), dim3(256), 0, s,
+                           static_cast<float *>(k_cache), static_cast<float *>(v_cache),
+                           static_cast<const float *>(k_new), static_cast<const float *>(v_new), d_slot_mapping,
+                           num_tokens, num_pages, page_size, num_kv_heads, head_dim);
+    } else {
+        hipLaunchKernelGGL(kv_append_kernel<uint16_t>, dim3(unsigned(blocks)), dim3(256), 0, s,
+                           static_cast<uint16_t *>(k_cache), static_cast<uint16_t *>(v_cache),
+                           static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new),
+                           d_slot_mapping, num_tokens, num_pages, page_size, num_kv_heads, head_dim);
+    }
+    return hipGetLastError() == hipSuccess ? CB_OK : CB_E_HIP;
+}
+
+extern "C" size_t cb_paged_attention_workspace_size(const cb_attn_args *a) {
+    if (!a) return 0;
+    const size_t n = size_t(a->plan_info.n_partials);
+    const size_t hq = size_t(a->shape.num_q_heads), d = size_t(a->shape.head_dim);
+    if (n == 0) return 0;
+    return align256(n * hq * d * sizeof(float)) + align256(n * hq * 2 * sizeof(float));
+}
+
+extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
+    if (!a || a->phases < 0 || a->phases > 15) return CB_E_INVAL;
+    const cb_attn_shape &sh = a->shape;
+    const cb_plan &pl = a->plan_info;
+    if (!shape_ok(sh)) return CB_E_UNSUPPORTED;
+    if (pl.n_decode < 0 || pl.n_prefill < 0 || pl.n_rowwise < 0 || pl.n_combine < 0 || pl.n_partials < 0)
+        return CB_E_INVAL;
+    const int64_t n_work = int64_t(pl.n_decode) + pl.n_prefill + pl.n_rowwise + pl.n_combine;
+    if (n_work == 0) return CB_OK;
+    if (!a->out || !a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->plan) return CB_E_INVAL;
+    if (a->num_pages < 1 || a->table_width <= pl.max_page_index) return CB_E_INVAL;
+    const int Hq = sh.num_q_heads, Hkv = sh.num_kv_heads, D = sh.head_dim;
+    const int G = Hq / Hkv;
+    const bool bf16 = sh.dtype == CB_DTYPE_BF16;
+    if ((pl.n_decode > 0 || pl.n_prefill > 0) && (!bf16 || sh.page_size < 8)) return CB_E_INVAL;
+    if (pl.n_decode > 0 && G > 16) return CB_E_INVAL;
+    if (pl.n_prefill > 0 && (G > kPfRows || kPfRows % G != 0 || pl.prefill_tokens != kPfRows / G))
+        return CB_E_INVAL;
+    const size_t need = cb_paged_attention_workspace_size(a);
+    if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return CB_E_WORKSPACE;
+    float *part_o = static_cast<float *>(a->workspace);
+    float *part_ml = need ? reinterpret_cast<float *>(static_cast<char *>(a->workspace) +
+                                                      align256(size_t(pl.n_partials) * Hq * D * sizeof(float)))
+                          : nullptr;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int Pl = ilog2(sh.page_size);
+    const float sl2e = a->scale * 1.4426950408889634f;   // scale * log2(e): softmax in base 2
+    const int32_t *plan = a->plan;
+    const int32_t ph = a->phases == 0 ? (CB_PHASE_DECODE | CB_PHASE_ROWWISE | CB_PHASE_PREFILL | CB_PHASE_COMBINE)
+                                      : a->phases;
+
+    if (pl.n_decode > 0 && (ph & CB_PHASE_DECODE)) {
+        const dim3 grid(unsigned(pl.n_decode), unsigned(Hkv));
+        const uint16_t *qq = static_cast<const uint16_t *>(a->q);
+        uint16_t *oo = static_cast<uint16_t *>(a->out);
+        const uint16_t *kk = static_cast<const uint16_t *>(a->k_cache);
+        const uint16_t *vv = static_cast<const uint16_t *>(a->v_cache);
+        if (D == 128)
+            hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,
+                               a->table_width, a->num_pages, plan + pl.off_decode, part_o, part_ml, Hq, Hkv, Pl, sl2e);
+        else
+            hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,
+                               a->table_width, a->num_pages, plan + pl.off_decode, part_o, part_ml, Hq, Hkv, Pl, sl2e);
+    }
+    if (pl.n_rowwise > 0 && (ph & CB_PHASE_ROWWISE)) {
+        const dim3 grid(unsigned(pl.n_rowwise), unsigned(Hkv), unsigned((G + 15) / 16));
+#define CB_ROWWISE(T, DD)                                                                                         \
+    hipLaunchKernelGGL((rowwise_kernel<T, DD>), grid, dim3(64), 0, s, static_cast<const T *>(a->q),              \
+                       static_cast<T *>(a->out), static_cast<const T *>(a->k_cache),                           \
+                       static_cast<const T *>(a->v_cache), a->block_table, a->table_width, a->num_pages,        \
+                       plan + pl.off_rowwise, part_o, part_ml, Hq, Hkv, Pl, sl2e)
+        if (bf16) {
+            if (D == 128) CB_ROWWISE(uint16_t, 128); else CB_ROWWISE(uint16_t, 64);
+        } else {
+            if (D == 128) CB_ROWWISE(float, 128); else CB_ROWWISE(float, 64);
+        }
+#undef CB_ROWWISE
+    }
+    if (pl.n_prefill > 0 && (ph & CB_PHASE_PREFILL)) {
+        const dim3 grid(unsigned(pl.n_prefill), unsigned(Hkv));
+        const uint16_t *qq = static_cast<const uint16_t *>(a->q);
+        uint16_t *oo = static_cast<uint16_t *>(a->out);
+        const uint16_t *kk = static_cast<const uint16_t *>(a->k_cache);
+        const uint16_t *vv = static_cast<const uint16_t *>(a->v_cache);
+        if (D == 128)
+            hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,
+                               a->table_width, a->num_pages, plan + pl.off_prefill, part_o, part_ml, Hq, Hkv, Pl,
+                               sl2e, sh.window_left);
+        else
+            hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,
+                               a->table_width, a->num_pages, plan + pl.off_prefill, part_o, part_ml, Hq, Hkv, Pl,
+                               sl2e, sh.window_left);
+    }
+    if (pl.n_combine > 0 && (ph & CB_PHASE_COMBINE)) {
+        if (bf16)
+            hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(unsigned(pl.n_combine)), dim3(256), 0, s,
+                               static_cast<uint16_t *>(a->out), part_o, part_ml, plan + pl.off_combine, Hq, D);
+        else
+            hipLaunchKernelGGL(combine_kernel<float>, dim3(unsigned(pl.n_combine)), dim3(256), 0, s,
+                               static_cast<float *>(a->out), part_o, part_ml, plan + pl.off_combine, Hq, D);
+    }
+    return hipGetLastError() == hipSuccess ? CB_OK : CB_E_HIP;
+}

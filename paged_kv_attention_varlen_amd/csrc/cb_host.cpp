@@ -1,0 +1,405 @@
+// Host half of the cb library: the step scheduler (cb_build_metadata) and the work planner (cb_plan_attention).
+//
+// Both are pure functions of their arguments: no allocation visible to the caller, no global state, no RNG.
+// Page allocation takes pages from the front of the caller's (already shuffled) free lists.
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "cb.h"
+
+namespace {
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Minimum ring (in pages) for a sliding layer: this step's queries at ctx .. ctx+q-1 still see keys back to
+// ctx-window_left, and the step writes keys up to ctx+q-1; those window_left+q positions, arbitrarily aligned,
+// touch at most (window_left + q + P - 2) / P + 1 pages, which must all sit in distinct ring slots.
+int64_t min_ring_pages(int32_t window_left, int32_t max_chunk, int32_t P) {
+    return (int64_t(window_left) + max_chunk + P - 2) / P + 1;
+}
+
+struct Scheduled {
+    int32_t req;                        // index into the caller's request array
+    int32_t q;                          // tokens of this step
+    int32_t new_from[CB_MAX_LAYERS];    // first index into the layer's free list taken by this row
+    int32_t new_count[CB_MAX_LAYERS];
+};
+
+}  // namespace
+
+extern "C" const char *cb_status_str(cb_status s) {
+    switch (s) {
+        case CB_OK: return "ok";
+        case CB_E_INVAL: return "invalid argument";
+        case CB_E_NOSPACE: return "no request could be scheduled: out of free pages";
+        case CB_E_CAPACITY: return "output buffer too small";
+        case CB_E_UNSUPPORTED: return "unsupported shape or dtype";
+        case CB_E_WORKSPACE: return "workspace missing or too small";
+        case CB_E_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int32_t cb_abi_version(void) { return CB_ABI_VERSION; }
+
+// ------------------------------------------------------------------------------------------------ scheduler
+
+extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const cb_sched_params *params,
+                                       const cb_layer_pool *layers, int32_t *out, int64_t out_capacity,
+                                       cb_step *step) {
+    if (!params || !layers || !step || n_reqs < 0 || (n_reqs > 0 && !reqs)) return CB_E_INVAL;
+    const int32_t P = params->page_size;
+    const int32_t L = params->n_layers;
+    const int32_t budget0 = params->max_batch_tokens;
+    const int32_t cap = params->max_requests;
+    if (P < 1 || budget0 < 1 || cap < 1 || L < 1 || L > CB_MAX_LAYERS) return CB_E_INVAL;
+    for (int l = 0; l < L; ++l) {
+        const cb_layer_pool &lay = layers[l];
+        if (lay.ring_len < 0 || lay.n_free < 0 || (lay.n_free > 0 && !lay.free_pages)) return CB_E_INVAL;
+        if (lay.ring_len > 0 && (lay.window_left < 0 || lay.ring_len < min_ring_pages(lay.window_left, budget0, P)))
+            return CB_E_INVAL;
+    }
+    for (int32_t i = 0; i < n_reqs; ++i) {
+        const cb_req &rq = reqs[i];
+        if (rq.state != CB_DECODING && rq.state != CB_PREFILLING && rq.state != CB_WAITING) return CB_E_INVAL;
+        if (rq.num_computed < 0 || rq.num_pending < 1) return CB_E_INVAL;
+        if (rq.state == CB_DECODING && rq.num_pending != 1) return CB_E_INVAL;
+        for (int l = 0; l < L; ++l) {
+            if (rq.n_pages[l] < 0 || (rq.n_pages[l] > 0 && !rq.pages[l])) return CB_E_INVAL;
+            if (layers[l].ring_len > 0) {
+                if (rq.state != CB_WAITING && rq.n_pages[l] != layers[l].ring_len) return CB_E_INVAL;
+            } else if (rq.n_pages[l] < ceil_div(rq.num_computed, P)) {
+                return CB_E_INVAL;
+            }
+        }
+    }
+
+    int32_t taken[CB_MAX_LAYERS] = {0, 0};
+    auto pages_needed = [&](const cb_req &rq, int32_t q, int32_t *need) {
+        for (int l = 0; l < L; ++l) {
+            const int64_t want = layers[l].ring_len > 0 ? layers[l].ring_len
+                                                        : ceil_div(int64_t(rq.num_computed) + q, P);
+            need[l] = int32_t(std::max<int64_t>(0, want - rq.n_pages[l]));
+        }
+    };
+    auto available = [&](const int32_t *need) {
+        for (int l = 0; l < L; ++l)
+            if (need[l] > layers[l].n_free - taken[l]) return false;
+        return true;
+    };
+
+    std::vector<Scheduled> rows;
+    std::vector<int32_t> stalled;
+    int32_t first_rejected = -1;
+    int32_t held = 0;
+    int32_t budget = budget0;
+    auto schedule = [&](int32_t i, int32_t q, const int32_t *need) {
+        Scheduled s{};
+        s.req = i;
+        s.q = q;
+        for (int l = 0; l < L; ++l) {
+            s.new_from[l] = taken[l];
+            s.new_count[l] = need[l];
+            taken[l] += need[l];
+        }
+        rows.push_back(s);
+        budget -= q;
+    };
+
+    // 1) active decodes
+    for (int32_t i = 0; i < n_reqs; ++i) {
+        if (reqs[i].state != CB_DECODING) continue;
+        if (int32_t(rows.size()) >= cap || budget < 1) break;
+        int32_t need[CB_MAX_LAYERS];
+        pages_needed(reqs[i], 1, need);
+        if (!available(need)) {
+            stalled.push_back(i);
+            continue;
+        }
+        schedule(i, 1, need);
+    }
+    const int32_t num_decodes = int32_t(rows.size());
+    // 2) active prefills continue where they stopped
+    for (int32_t i = 0; i < n_reqs; ++i) {
+        if (reqs[i].state != CB_PREFILLING) continue;
+        if (int32_t(rows.size()) >= cap || budget < 1) break;
+        const int32_t q = std::min(reqs[i].num_pending, budget);
+        int32_t need[CB_MAX_LAYERS];
+        pages_needed(reqs[i], q, need);
+        if (!available(need)) {
+            stalled.push_back(i);
+            continue;
+        }
+        schedule(i, q, need);
+    }
+    // 3) admission of waiting requests, in arrival order
+    for (int32_t i = 0; i < n_reqs; ++i) {
+        if (reqs[i].state != CB_WAITING) continue;
+        if (int32_t(rows.size()) >= cap || budget < 1) break;
+        bool low = false;
+        for (int l = 0; l < L; ++l) {
+            const cb_layer_pool &lay = layers[l];
+            if (lay.pool_pages > 0 &&
+                double(lay.n_free - taken[l]) < double(params->safety_margin) * double(lay.pool_pages))
+                low = true;
+        }
+        if (low) {
+            held = 1;
+            break;
+        }
+        const int32_t q = std::min(reqs[i].num_pending, budget);
+        int32_t need[CB_MAX_LAYERS];
+        pages_needed(reqs[i], q, need);
+        if (!available(need)) {
+            first_rejected = i;
+            break;
+        }
+        schedule(i, q, need);
+    }
+
+    // ---- sizes and offsets of the packed output
+    const int32_t N = int32_t(rows.size());
+    int64_t T = 0;
+    int32_t max_q = 0, max_seq = 0;
+    for (const Scheduled &s : rows) {
+        T += s.q;
+        max_q = std::max(max_q, s.q);
+        max_seq = std::max(max_seq, reqs[s.req].num_computed + s.q);
+    }
+    if (T > INT32_MAX) return CB_E_INVAL;
+    std::memset(step, 0, sizeof(*step));
+    step->num_reqs = N;
+    step->num_tokens = int32_t(T);
+    step->num_decodes = num_decodes;
+    step->max_q_len = max_q;
+    step->max_seq_len = max_seq;
+    step->n_stalled = int32_t(stalled.size());
+    step->first_rejected = first_rejected;
+    step->held_by_margin = held;
+    int64_t off = 0;
+    step->off_query_start_loc = off; off += N + 1;
+    step->off_seq_lens = off;        off += N;
+    step->off_req_index = off;       off += N;
+    step->off_stalled = off;         off += int64_t(stalled.size());
+    for (int l = 0; l < L; ++l) {
+        step->used_pages[l] = taken[l];
+        const int32_t width = layers[l].ring_len > 0 ? layers[l].ring_len : int32_t(ceil_div(max_seq, P));
+        step->table_width[l] = width;
+        step->off_block_table[l] = off;  off += int64_t(N) * width;
+        step->off_slot_mapping[l] = off; off += T;
+        step->off_ring_len[l] = off;     off += N;
+    }
+    step->used = off;
+    if (off > out_capacity || !out) return CB_E_CAPACITY;
+
+    // ---- ragged metadata
+    int32_t *qsl = out + step->off_query_start_loc;
+    int32_t *seq = out + step->off_seq_lens;
+    int32_t *idx = out + step->off_req_index;
+    qsl[0] = 0;
+    for (int32_t r = 0; r < N; ++r) {
+        qsl[r + 1] = qsl[r] + rows[r].q;
+        seq[r] = reqs[rows[r].req].num_computed + rows[r].q;
+        idx[r] = rows[r].req;
+    }
+    std::copy(stalled.begin(), stalled.end(), out + step->off_stalled);
+
+    // ---- per layer: block table, slot mapping, ring length
+    for (int l = 0; l < L; ++l) {
+        const cb_layer_pool &lay = layers[l];
+        const int32_t width = step->table_width[l];
+        const int32_t R = lay.ring_len;
+        int32_t *table = out + step->off_block_table[l];
+        int32_t *slots = out + step->off_slot_mapping[l];
+        int32_t *rlen = out + step->off_ring_len[l];
+        for (int32_t r = 0; r < N; ++r) {
+            const Scheduled &s = rows[r];
+            const cb_req &rq = reqs[s.req];
+            int32_t *row = table + int64_t(r) * width;
+            // the row's pages: those owned, then those just taken from the free list
+            const int32_t used = R > 0 ? R : int32_t(ceil_div(seq[r], P));
+            for (int32_t b = 0; b < width; ++b) {
+                int32_t page = params->pad_page;
+                if (b < used) {
+                    page = b < rq.n_pages[l] ? rq.pages[l][b]
+                                             : lay.free_pages[s.new_from[l] + (b - rq.n_pages[l])];
+                }
+                row[b] = page;
+            }
+            rlen[r] = R;
+            for (int32_t j = 0; j < s.q; ++j) {
+                const int64_t pos = int64_t(rq.num_computed) + j;
+                const int64_t logical = pos / P;
+                const int32_t page = R > 0 ? row[logical % R] : row[logical];
+                slots[qsl[r] + j] = int32_t(int64_t(page) * P + pos % P);
+            }
+        }
+    }
+    const bool blocked = !stalled.empty() || first_rejected >= 0;
+    return (N == 0 && blocked) ? CB_E_NOSPACE : CB_OK;
+}
+
+// -------------------------------------------------------------------------------------------------- planner
+//
+// Work items, 8 int32 each:
+//   decode / row-wise item:  {row, token, pos, kv_lo, kv_hi, slot, ring_len, 0}
+//   prefill tile item:       {row, token0, pos0, q_count, kv_lo, kv_hi, slot_base, ring_len}
+// Merge item, 4 int32:       {token, first_slot, n_splits, slot_stride}
+// [kv_lo, kv_hi) is the item's key range (absolute positions). slot < 0: the item owns the whole visible range of
+// its rows and writes the output; otherwise it writes unnormalised partial results into workspace slots.
+
+namespace {
+
+constexpr int kPrefillRows = 128;   // query rows (token x grouped head) of one prefill tile
+constexpr int kNumCUs = 256;
+
+struct Item {
+    int32_t v[8];
+};
+
+}  // namespace
+
+extern "C" cb_status cb_plan_attention(const int32_t *qsl, const int32_t *seq_lens, const int32_t *ring_len,
+                                       int32_t N, const cb_attn_shape *sh, int32_t *out, int64_t out_capacity,
+                                       cb_plan *plan) {
+    if (!sh || !plan || N < 0 || (N > 0 && (!qsl || !seq_lens))) return CB_E_INVAL;
+    const int32_t Hq = sh->num_q_heads, Hkv = sh->num_kv_heads, D = sh->head_dim, P = sh->page_size;
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || sh->window_left < -1) return CB_E_INVAL;
+    if (sh->decode_split < 0 || sh->decode_split % 64 != 0) return CB_E_INVAL;
+    if (sh->prefill_split < 0 || sh->prefill_split % 64 != 0) return CB_E_INVAL;
+    if ((D != 64 && D != 128) || !is_pow2(P) || P > 256) return CB_E_UNSUPPORTED;
+    if (sh->dtype != CB_DTYPE_F32 && sh->dtype != CB_DTYPE_BF16) return CB_E_UNSUPPORTED;
+    if (N > 0 && qsl[0] != 0) return CB_E_INVAL;
+    for (int32_t r = 0; r < N; ++r) {
+        const int32_t q = qsl[r + 1] - qsl[r];
+        if (q < 0 || seq_lens[r] < q) return CB_E_INVAL;
+        if (ring_len && ring_len[r] < 1) return CB_E_INVAL;
+    }
+    const int32_t G = Hq / Hkv;
+    const int32_t W = sh->window_left;
+    const bool bf16 = sh->dtype == CB_DTYPE_BF16;
+    const bool fast_decode = bf16 && P >= 8 && G <= 16;
+    const bool fast_prefill = bf16 && P >= 8 && G <= kPrefillRows && kPrefillRows % G == 0;
+    const int32_t tile_tokens = fast_prefill ? kPrefillRows / G : 0;
+    auto lo_of = [&](int64_t pos) -> int64_t { return W < 0 ? 0 : std::max<int64_t>(0, pos - W); };
+
+    // ---- split sizes. Decode: enough (row, split, kv head) work groups to give every CU several; prefill: tiles
+    // with long key ranges are cut so that no work group carries many times the average work.
+    int64_t dec_keys = 0, tile_work = 0, n_tiles = 0;
+    for (int32_t r = 0; r < N; ++r) {
+        const int32_t q = qsl[r + 1] - qsl[r];
+        const int64_t ctx = int64_t(seq_lens[r]) - q;
+        const bool as_rows = (q == 1) ? !fast_decode : !fast_prefill;
+        if (q == 1 || as_rows) {
+            for (int32_t i = 0; i < q; ++i) dec_keys += ctx + i + 1 - lo_of(ctx + i);
+        } else {
+            for (int32_t i0 = 0; i0 < q; i0 += tile_tokens) {
+                const int64_t hi = ctx + std::min(q, i0 + tile_tokens);
+                tile_work += hi - lo_of(ctx + i0);
+                ++n_tiles;
+            }
+        }
+    }
+    int32_t S = sh->decode_split;
+    if (S == 0) {
+        const int64_t target_groups = 8 * kNumCUs;                       // work groups across all kv heads
+        const int64_t per = ceil_div(dec_keys * Hkv, target_groups);
+        S = int32_t(std::min<int64_t>(4096, std::max<int64_t>(256, ceil_div(per, 256) * 256)));
+    }
+    int32_t PS = sh->prefill_split;
+    if (PS == 0) {
+        const int64_t groups = std::max<int64_t>(1, n_tiles * Hkv);
+        const int64_t avg = ceil_div(tile_work, std::max<int64_t>(1, n_tiles));
+        // aim for >= 2 groups per CU; never cut below 512 keys
+        const int64_t want = std::max<int64_t>(1, ceil_div(2 * kNumCUs, groups));
+        const int64_t per = ceil_div(avg, want);
+        PS = int32_t(std::min<int64_t>(1 << 20, std::max<int64_t>(512, ceil_div(per, 64) * 64)));
+    }
+
+    std::vector<Item> dec, pre, rowwise;
+    std::vector<int32_t> comb;
+    int64_t slots = 0;
+    int64_t max_block = -1;
+    auto split_row = [&](std::vector<Item> &dst, int32_t r, int32_t t, int64_t pos, int32_t ring) {
+        const int64_t lo = lo_of(pos), hi = pos + 1;
+        const int64_t first = (lo / S) * S;
+        const int64_t n = ceil_div(hi - first, S);
+        const int64_t base = n > 1 ? slots : -1;
+        for (int64_t s = 0; s < n; ++s) {
+            const int64_t a = std::max(lo, first + s * S), b = std::min(hi, first + (s + 1) * S);
+            Item it{{r, t, int32_t(pos), int32_t(a), int32_t(b), int32_t(n > 1 ? base + s : -1), ring, 0}};
+            dst.push_back(it);
+        }
+        if (n > 1) {
+            comb.insert(comb.end(), {t, int32_t(base), int32_t(n), 1});
+            slots += n;
+        }
+        max_block = std::max<int64_t>(max_block, ring > 0 ? ring - 1 : (hi - 1) / P);
+    };
+
+    for (int32_t r = 0; r < N; ++r) {
+        const int32_t q = qsl[r + 1] - qsl[r];
+        if (q == 0) continue;
+        const int64_t ctx = int64_t(seq_lens[r]) - q;
+        const int32_t ring = ring_len ? ring_len[r] : 0;
+        if (q == 1 && fast_decode) {
+            split_row(dec, r, qsl[r], ctx, ring);
+        } else if (q > 1 && fast_prefill) {
+            for (int32_t i0 = 0; i0 < q; i0 += tile_tokens) {
+                const int32_t qc = std::min(tile_tokens, q - i0);
+                const int64_t pos0 = ctx + i0;
+                const int64_t lo = lo_of(pos0), hi = pos0 + qc;
+                const int64_t first = (lo / PS) * PS;
+                const int64_t n = ceil_div(hi - first, PS);
+                const int64_t base = n > 1 ? slots : -1;
+                for (int64_t s = 0; s < n; ++s) {
+                    const int64_t a = std::max(lo, first + s * PS), b = std::min(hi, first + (s + 1) * PS);
+                    Item it{{r, qsl[r] + i0, int32_t(pos0), qc, int32_t(a), int32_t(b),
+                             int32_t(n > 1 ? base + s * qc : -1), ring}};
+                    pre.push_back(it);
+                }
+                if (n > 1) {
+                    for (int32_t i = 0; i < qc; ++i)
+                        comb.insert(comb.end(), {qsl[r] + i0 + i, int32_t(base + i), int32_t(n), qc});
+                    slots += n * qc;
+                }
+                max_block = std::max<int64_t>(max_block, ring > 0 ? ring - 1 : (hi - 1) / P);
+            }
+        } else {
+            for (int32_t i = 0; i < q; ++i) split_row(rowwise, r, qsl[r] + i, ctx + i, ring);
+        }
+    }
+    if (slots > INT32_MAX / 2) return CB_E_UNSUPPORTED;
+
+    std::memset(plan, 0, sizeof(*plan));
+    plan->n_decode = int32_t(dec.size());
+    plan->n_prefill = int32_t(pre.size());
+    plan->n_rowwise = int32_t(rowwise.size());
+    plan->n_combine = int32_t(comb.size() / 4);
+    plan->n_partials = int32_t(slots);
+    plan->decode_split = S;
+    plan->prefill_split = PS;
+    plan->prefill_tokens = tile_tokens;
+    plan->num_tokens = N > 0 ? qsl[N] : 0;
+    plan->max_page_index = int32_t(max_block);
+    int64_t off = 0;
+    plan->off_decode = off;  off += 8 * int64_t(dec.size());
+    plan->off_prefill = off; off += 8 * int64_t(pre.size());
+    plan->off_rowwise = off; off += 8 * int64_t(rowwise.size());
+    plan->off_combine = off; off += int64_t(comb.size());
+    plan->used = off;
+    if (off > out_capacity || (off > 0 && !out)) return CB_E_CAPACITY;
+    auto put = [&](const std::vector<Item> &v, int64_t at) {
+        for (size_t k = 0; k < v.size(); ++k) std::memcpy(out + at + 8 * int64_t(k), v[k].v, sizeof(Item));
+    };
+    put(dec, plan->off_decode);
+    put(pre, plan->off_prefill);
+    put(rowwise, plan->off_rowwise);
+    if (!comb.empty()) std::memcpy(out + plan->off_combine, comb.data(), comb.size() * sizeof(int32_t));
+    return CB_OK;
+}

@@ -1,0 +1,190 @@
+"""Device driver for one mixed step: metadata -> plans -> one host-to-device copy -> KV append -> attention.
+
+`Step` strings the library's calls together for one or two layer types (a full layer, optionally a sliding layer)
+that share the step's schedule. `Step.from_workload` builds the device state of a seeded synthetic workload: the
+KV caches (every page first filled with NaN, so pages that must never be read poison any output that reads them),
+the history of every admitted request written through cb_kv_append, and the step's new Q/K/V rows.
+
+History convention (setup, not part of the method): full layers get positions 0 .. context-1; sliding layers get
+only the positions this step's queries can still see, max(0, context - window_left) .. context-1, so older ring
+slots stay NaN.
+"""
+from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+from typing import List, Optional
+
+import numpy as np
+
+from . import (CB_PHASE_COMBINE, CB_PHASE_DECODE, CB_PHASE_PREFILL, CB_PHASE_ROWWISE, AttnPlan, build_metadata,
+               kv_append, paged_attention, plan_attention, workspace_size)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+@dataclass
+class LayerState:
+    name: str
+    window_left: int
+    ring: bool
+    k_cache: object            # torch [pages, Hkv, P, D]
+    v_cache: object            # torch [pages, Hkv, D, P]
+    plan: AttnPlan
+    plan_dev: object           # torch int32 view into the packed device buffer
+    block_table: object        # torch int32 [N, width]
+    slot_mapping: object       # torch int32 [T]
+    q: object                  # torch [T, Hq, D]
+    k_new: object              # torch [T, Hkv, D]
+    v_new: object
+    out: object                # torch [T, Hq, D]
+    workspace: Optional[object]
+
+
+class Step:
+    """One scheduled step on the device. Call `run()` (append + attention for every layer)."""
+
+    def __init__(self, sched: dict, layers: List[LayerState], scale: float, dtype, Hq: int, Hkv: int, D: int, P: int):
+        self.sched = sched
+        self.layers = layers
+        self.scale = scale
+        self.dtype = dtype
+        self.Hq, self.Hkv, self.D, self.P = Hq, Hkv, D, P
+
+    # ---------------------------------------------------------------------------------------------- execution
+    def append(self, l: int) -> None:
+        L = self.layers[l]
+        kv_append(L.k_cache, L.v_cache, L.k_new, L.v_new, L.slot_mapping)
+
+    def attend(self, l: int, phases: int = 0) -> None:
+        L = self.layers[l]
+        paged_attention(L.out, L.q, L.k_cache, L.v_cache, L.block_table, L.plan, L.plan_dev, self.scale,
+                        L.workspace, phases=phases)
+
+    def run(self) -> None:
+        for l in range(len(self.layers)):
+            self.append(l)
+            self.attend(l)
+
+    PHASE_DECODE = CB_PHASE_DECODE
+    PHASE_REST = CB_PHASE_ROWWISE | CB_PHASE_PREFILL | CB_PHASE_COMBINE
+
+    # ------------------------------------------------------------------------------------------- construction
+    @classmethod
+    def from_workload(cls, w, device: str = "cuda", decode_split: int = 0, prefill_split: int = 0,
+                      threads: int = 8, verbose: bool = False) -> "Step":
+        torch = _torch()
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        P, Hq, Hkv, D = w.page_size, w.Hq, w.Hkv, w.D
+        pools = [{"ring_len": lay.ring_len, "window_left": lay.window_left,
+                  "pool_pages": lay.num_pages - len(lay.padding_pages), "free_pages": lay.free_pages}
+                 for lay in w.layers]
+        pad = w.layers[0].padding_pages[0] if w.layers[0].padding_pages else 0
+        sched = build_metadata(w.requests, pools, w.max_batch_tokens, w.max_requests, P, w.safety_margin, pad)
+        if sched["status"] != 0:
+            raise RuntimeError(f"cb_build_metadata returned status {sched['status']}")
+        N, T = sched["num_reqs"], sched["num_tokens"]
+        qsl, seq, idx = sched["query_start_loc"], sched["seq_lens"], sched["req_index"]
+
+        # one packed int32 host buffer -> one H2D copy: per layer block table, slot mapping, plan
+        plans, parts = [], []
+        for l, lay in enumerate(w.layers):
+            L = sched["layers"][l]
+            ring = L["ring_len"] if lay.ring_len > 0 else None
+            plan = plan_attention(qsl, seq, ring, Hq, Hkv, D, P, dt, lay.window_left, decode_split, prefill_split)
+            plans.append(plan)
+            parts += [L["block_table"].reshape(-1), L["slot_mapping"], plan.buffer]
+        offs = np.cumsum([0] + [p.size for p in parts])
+        packed = torch.from_numpy(np.concatenate(parts).astype(np.int32)).to(device)
+
+        def view(k, shape=None):
+            t = packed[offs[k]:offs[k + 1]]
+            return t.view(*shape) if shape is not None else t
+
+        layers = []
+        pool = ThreadPoolExecutor(max(1, threads))
+        for l, lay in enumerate(w.layers):
+            L = sched["layers"][l]
+            kc = torch.full((lay.num_pages, Hkv, P, D), float("nan"), dtype=dt, device=device)
+            vc = torch.full((lay.num_pages, Hkv, D, P), float("nan"), dtype=dt, device=device)
+            _fill_history(w, l, kc, vc, pool, device, dt)
+            q = torch.empty((T, Hq, D), dtype=dt)
+            kn = torch.empty((T, Hkv, D), dtype=dt)
+            vn = torch.empty((T, Hkv, D), dtype=dt)
+
+            def new_rows(r):
+                qs, qe = int(qsl[r]), int(qsl[r + 1])
+                ctx = int(seq[r]) - (qe - qs)
+                i = int(idx[r])
+                return qs, qe, [w.values(n, i, l, ctx, ctx + qe - qs) for n in ("q", "k", "v")]
+
+            for qs, qe, (a, b, c) in pool.map(new_rows, range(N)):
+                q[qs:qe] = torch.from_numpy(a).to(dt)
+                kn[qs:qe] = torch.from_numpy(b).to(dt)
+                vn[qs:qe] = torch.from_numpy(c).to(dt)
+            plan = plans[l]
+            ws_bytes = workspace_size(plan)
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device) if ws_bytes else None
+            layers.append(LayerState(lay.name, lay.window_left, lay.ring_len > 0, kc, vc, plan,
+                                     view(3 * l + 2), view(3 * l, (N, L["width"])), view(3 * l + 1),
+                                     q.to(device), kn.to(device), vn.to(device),
+                                     torch.empty((T, Hq, D), dtype=dt, device=device), ws))
+            if verbose:
+                print(f"[step] layer {lay.name}: plan {plan.counts()}", flush=True)
+        pool.shutdown()
+        torch.cuda.synchronize()
+        return cls(sched, layers, w.scale, dt, Hq, Hkv, D, P)
+
+
+def history_slots(pages: np.ndarray, lo: int, hi: int, P: int, ring_len: int) -> np.ndarray:
+    """Cache slots (page * P + offset) of positions lo .. hi-1 of a request owning `pages` (logical order, or a
+    ring of ring_len pages)."""
+    pos = np.arange(lo, hi, dtype=np.int64)
+    blk = pos // P
+    if ring_len > 0:
+        blk = blk % ring_len
+    return (pages.astype(np.int64)[blk] * P + pos % P).astype(np.int32)
+
+
+def _fill_history(w, l: int, kc, vc, pool, device, dt, chunk_tokens: int = 1 << 18) -> None:
+    """Write every admitted request's history into layer l's caches through cb_kv_append."""
+    torch = _torch()
+    lay = w.layers[l]
+    P = w.page_size
+    jobs = []
+    for i, rq in enumerate(w.requests):
+        if rq.num_computed == 0 or len(rq.pages[l]) == 0:
+            continue
+        lo = 0 if lay.window_left < 0 else max(0, rq.num_computed - lay.window_left)
+        jobs.append((i, lo, rq.num_computed))
+
+    def gen(job):
+        i, lo, hi = job
+        k = w.values("k", i, l, lo, hi)
+        v = w.values("v", i, l, lo, hi)
+        s = history_slots(np.asarray(w.requests[i].pages[l]), lo, hi, P, lay.ring_len)
+        return torch.from_numpy(k).to(dt), torch.from_numpy(v).to(dt), torch.from_numpy(s)
+
+    batch, n = [], 0
+
+    def flush():
+        nonlocal batch, n
+        if not batch:
+            return
+        k = torch.cat([b[0] for b in batch]).to(device)
+        v = torch.cat([b[1] for b in batch]).to(device)
+        s = torch.cat([b[2] for b in batch]).to(device)
+        kv_append(kc, vc, k, v, s)
+        batch, n = [], 0
+
+    group = 16   # requests generated ahead of the copies, bounding host memory
+    for g0 in range(0, len(jobs), group):
+        for res in pool.map(gen, jobs[g0:g0 + group]):
+            batch.append(res)
+            n += res[0].shape[0]
+            if n >= chunk_tokens:
+                flush()
+    flush()

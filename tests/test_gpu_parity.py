@@ -1,0 +1,177 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Reduced workloads are compared element by element on every output row and every cache page; the full-size
+workloads -- in the launch configuration the benchmark times -- on sampled rows and on the pages the step's append
+touched. Tolerances: fp32 max-abs 1e-5; bf16 max-abs 2e-2 and mean-abs 2e-3; append bit-exact.
+"""
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import reference as R
+from synth import DECODING, PREFILLING, WAITING, make_workload
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_attention_varlen_amd import load_library
+    load_library()
+    return torch
+
+
+def _run(w, **kw):
+    from paged_kv_attention_varlen_amd.step import Step
+    print(f"[gpu] {w.name} {kw}", flush=True)
+    st = Step.from_workload(w, **kw)
+    st.run()
+    import torch
+    torch.cuda.synchronize()
+    return st
+
+
+def _check_pages(w, st, layer, pages=None):
+    ids, k_ref, v_ref = R.pages_reference(w, layer, R.schedule(w), pages)
+    k, v = H.logical_cache(st, layer)
+    assert H.same_bits(k[ids], k_ref), "K cache differs"
+    assert H.same_bits(v[ids], v_ref), "V cache differs"
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_reduced_workload_all_rows_and_pages(torch_gpu, idx):
+    w = make_workload(idx, mini=True)
+    st = _run(w)
+    for l in range(len(w.layers)):
+        mx, mean = H.compare(w, st, l, label=f"w{idx} reduced layer {l}")
+        print(f"  layer {l}: max {mx:.3g} mean {mean:.3g}", flush=True)
+        _check_pages(w, st, l)
+
+
+def _sample_tokens(sched, rng, n_dec=12, per_chunk=6):
+    qsl = sched["query_start_loc"]
+    seq = sched["seq_lens"]
+    nd = sched["num_decodes"]
+    toks = set()
+    if nd:
+        dec = np.arange(nd)
+        toks |= {int(qsl[int(np.argmax(seq[:nd]))]), int(qsl[int(np.argmin(seq[:nd]))])}
+        toks |= {int(qsl[r]) for r in rng.choice(dec, size=min(n_dec, nd), replace=False)}
+    for r in range(nd, sched["num_reqs"]):
+        a, b = int(qsl[r]), int(qsl[r + 1])
+        toks |= {a, b - 1}
+        toks |= {int(t) for t in rng.integers(a, b, size=min(per_chunk, b - a))}
+    return sorted(toks)
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_full_workload_sampled_rows(torch_gpu, idx):
+    w = make_workload(idx)
+    st = _run(w)
+    rng = np.random.default_rng(100 + idx)
+    sched = R.schedule(w)
+    toks = _sample_tokens(sched, rng)
+    for l in range(len(w.layers)):
+        out = st.layers[l].out
+        assert bool(torch_gpu.isfinite(out.float()).all()), "non-finite output somewhere"
+        mx, mean = H.compare(w, st, l, toks, label=f"w{idx} full layer {l}")
+        print(f"  layer {l}: {len(toks)} rows, max {mx:.3g} mean {mean:.3g}", flush=True)
+        touched = set((sched["layers"][l]["slot_mapping"] // w.page_size).tolist())
+        _check_pages(w, st, l, sorted(touched)[:64])
+
+
+def test_workload_1_matches_explicit_mask(torch_gpu):
+    """The tiny A/B/C step against dense attention under the explicit (T,T) block-diagonal mask."""
+    w = make_workload(1)
+    st = _run(w)
+    sched = R.schedule(w)
+    q, k, v = R.step_inputs(w, 0, sched)
+    ref = A.masked_attention(q, k, v, A.block_diagonal_causal_mask(sched["query_start_loc"]), w.scale)
+    got = H.gpu_rows(st, 0, range(sched["num_tokens"]))
+    assert np.abs(got - ref).max() <= H.TOL_F32_MAX
+
+
+EDGE = {
+    "decode ctx0 and page boundaries P16": dict(reqs=[(WAITING, 0, 1), (DECODING, 16, 1), (DECODING, 15, 1),
+                                                      (DECODING, 31, 1), (DECODING, 32, 1), (DECODING, 1, 1)]),
+    "page 8": dict(reqs=[(DECODING, 100, 1), (PREFILLING, 37, 45), (WAITING, 0, 70)], P=8),
+    "page 64": dict(reqs=[(DECODING, 300, 1), (PREFILLING, 100, 90), (WAITING, 0, 129)], P=64),
+    "page 256": dict(reqs=[(DECODING, 700, 1), (PREFILLING, 300, 300), (WAITING, 0, 257)], P=256),
+    "head dim 64": dict(reqs=[(DECODING, 900, 1), (PREFILLING, 200, 150), (WAITING, 0, 65)], D=64),
+    "group 16 (decode fast path limit)": dict(reqs=[(DECODING, 500, 1), (PREFILLING, 64, 20)], Hq=32, Hkv=2),
+    "group 32 (decode via per-token kernel)": dict(reqs=[(DECODING, 500, 1), (PREFILLING, 64, 20)], Hq=32, Hkv=1),
+    "MHA group 1": dict(reqs=[(DECODING, 333, 1), (WAITING, 0, 200)], Hq=4, Hkv=4),
+    "bf16 page 4 (per-token kernel)": dict(reqs=[(DECODING, 77, 1), (PREFILLING, 10, 30)], P=4),
+    "sliding window 0": dict(reqs=[(DECODING, 50, 1), (PREFILLING, 40, 33)], window_left=0, ring_len=8, budget=64),
+    "sliding window 1": dict(reqs=[(DECODING, 50, 1), (PREFILLING, 40, 33)], window_left=1, ring_len=8, budget=64),
+    "sliding window 100 P16": dict(reqs=[(DECODING, 1000, 1), (PREFILLING, 500, 200), (WAITING, 0, 150)],
+                                   window_left=100, ring_len=24, budget=256),
+    "fp32 long rows with splits": dict(reqs=[(DECODING, 2000, 1), (PREFILLING, 500, 60), (WAITING, 0, 40)],
+                                       dtype="f32", Hq=4, Hkv=2, D=64, P=16),
+    "many splits": dict(reqs=[(DECODING, 3000, 1), (DECODING, 70, 1), (PREFILLING, 1000, 300)],
+                        decode_split=64, prefill_split=64),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_cases(torch_gpu, name):
+    cfg = dict(EDGE[name])
+    reqs = cfg.pop("reqs")
+    ds = cfg.pop("decode_split", 0)
+    ps = cfg.pop("prefill_split", 0)
+    w = H.custom_workload(reqs, name=name, **cfg)
+    st = _run(w, decode_split=ds, prefill_split=ps)
+    print(f"  plan {st.layers[0].plan.counts()}", flush=True)
+    H.compare(w, st, 0, label=name)
+    _check_pages(w, st, 0)
+
+
+def test_zero_length_rows_through_the_abi(torch_gpu):
+    """Rows with q_len 0 produce nothing; their neighbours are unaffected (metadata built by hand, not scheduled)."""
+    import torch
+    import paged_kv_attention_varlen_amd as cb
+    rng = np.random.default_rng(5)
+    P, Hq, Hkv, D, n_pages = 16, 8, 2, 128, 40
+    qsl = np.array([0, 1, 1, 4, 4], np.int32)
+    seq = np.array([20, 9, 35, 1], np.int32)
+    width = 3
+    table = rng.permutation(np.arange(2, n_pages))[:4 * width].reshape(4, width).astype(np.int32)
+    kc = np.full((n_pages, P, Hkv, D), np.nan, np.float32)
+    vc = np.full((n_pages, P, Hkv, D), np.nan, np.float32)
+    from synth import round_to_bf16
+    for r in range(4):
+        for pos in range(int(seq[r])):
+            s = A.slot_of(table[r], pos, P)
+            kc[s // P, s % P] = round_to_bf16(rng.standard_normal((Hkv, D)).astype(np.float32))
+            vc[s // P, s % P] = round_to_bf16(rng.standard_normal((Hkv, D)).astype(np.float32))
+    q = round_to_bf16(rng.standard_normal((4, Hq, D)).astype(np.float32))
+    ref = A.paged_attention(q, kc.astype(np.float64), vc.astype(np.float64), qsl, seq, table, P, 0.1)
+    dev = "cuda"
+    kd = torch.from_numpy(kc.transpose(0, 2, 1, 3).copy()).to(torch.bfloat16).to(dev)
+    vd = torch.from_numpy(vc.transpose(0, 2, 3, 1).copy()).to(torch.bfloat16).to(dev)
+    qd = torch.from_numpy(q).to(torch.bfloat16).to(dev)
+    out = torch.full_like(qd, float("nan"))
+    plan = cb.plan_attention(qsl, seq, None, Hq, Hkv, D, P, "bf16", -1, 64, 64)
+    pd = torch.from_numpy(plan.buffer).to(dev)
+    ws = torch.empty(max(1, cb.workspace_size(plan)), dtype=torch.uint8, device=dev)
+    cb.paged_attention(out, qd, kd, vd, torch.from_numpy(table).to(dev), plan, pd, 0.1, ws)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.abs(got - ref).max() <= H.TOL_BF16_MAX
+
+
+def test_deterministic_and_batch_invariant(torch_gpu):
+    """Same inputs twice: identical bits. With fixed split sizes, a request's rows do not depend on its batch."""
+    reqs = [(DECODING, 1500, 1), (DECODING, 700, 1), (PREFILLING, 300, 100), (WAITING, 0, 90)]
+    w = H.custom_workload(reqs, name="batch")
+    a = _run(w, decode_split=256, prefill_split=512)
+    b = _run(w, decode_split=256, prefill_split=512)
+    assert torch_gpu.equal(a.layers[0].out, b.layers[0].out)
+    alone = H.custom_workload(reqs[:1], name="alone", n_pages=w.layers[0].num_pages - 2)
+    alone.requests[0].pages = [w.requests[0].pages[0]]
+    c = _run(alone, decode_split=256, prefill_split=512)
+    assert torch_gpu.equal(a.layers[0].out[0], c.layers[0].out[0])

@@ -1,0 +1,110 @@
+"""cb_plan_attention: every query row's visible key range is covered exactly once by its work items, split rows have
+one merge entry naming exactly their partial slots, and unsupported shapes fall back to per-token items."""
+import numpy as np
+import pytest
+
+import paged_kv_attention_varlen_amd as cb
+
+
+def _cover_check(qsl, seq, ring, plan, window):
+    T = int(qsl[-1])
+    dec, pre, row, comb = (plan.items(k) for k in ("decode", "prefill", "rowwise", "combine"))
+    per_tok = {t: [] for t in range(T)}
+    for it in np.concatenate([dec, row]) if len(dec) + len(row) else []:
+        r, t, pos, a, b, slot, rl, _ = (int(x) for x in it)
+        per_tok[t].append((a, b, slot, 1))
+        assert rl == (0 if ring is None else ring[r])
+    for it in pre:
+        r, t0, pos0, qc, a, b, sb, rl = (int(x) for x in it)
+        assert 1 <= qc <= plan.info.prefill_tokens
+        for i in range(qc):
+            per_tok[t0 + i].append((a, b, -1 if sb < 0 else sb + i, qc))
+    merges = {int(c[0]): c for c in comb}
+    slots_seen = set()
+    for r in range(len(seq)):
+        q = int(qsl[r + 1] - qsl[r])
+        ctx = int(seq[r]) - q
+        for i in range(q):
+            t = int(qsl[r]) + i
+            pos = ctx + i
+            lo = 0 if window < 0 else max(0, pos - window)
+            items = per_tok[t]
+            assert items, t
+            cov = np.zeros(pos + 1, dtype=int)
+            for a, b, slot, _ in items:
+                a2, b2 = max(a, lo), min(b, pos + 1)
+                if b2 > a2:
+                    cov[a2:b2] += 1
+            assert (cov[lo:] == 1).all() and (cov[:lo] == 0).all(), (t, items)
+            if len(items) == 1:
+                assert items[0][2] == -1 and t not in merges
+            else:
+                m = merges[t]
+                n, first, stride = int(m[2]), int(m[1]), int(m[3])
+                assert n == len(items)
+                want = sorted(first + s * stride for s in range(n))
+                assert sorted(x[2] for x in items) == want
+                assert not (set(want) & slots_seen)
+                slots_seen |= set(want)
+    assert all(s < plan.info.n_partials for s in slots_seen)
+
+
+def _random(rng):
+    N = int(rng.integers(1, 14))
+    q = rng.choice([0, 1, 1, 1, 2, 5, 33, 130, 300], size=N)
+    ctx = rng.integers(0, 3000, size=N)
+    qsl = np.concatenate([[0], np.cumsum(q)]).astype(np.int32)
+    return qsl, (ctx + q).astype(np.int32)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_plan_covers_every_row_exactly_once(seed):
+    rng = np.random.default_rng(seed)
+    qsl, seq = _random(rng)
+    window = int(rng.choice([-1, -1, 0, 100, 1000]))
+    ring = None if window < 0 else np.full(len(seq), 50, np.int32)
+    Hkv = int(rng.choice([1, 2, 8]))
+    G = int(rng.choice([1, 4, 8, 32]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    P = int(rng.choice([2, 8, 16, 32]))
+    ds = int(rng.choice([0, 64, 256]))
+    ps = int(rng.choice([0, 64, 512]))
+    plan = cb.plan_attention(qsl, seq, ring, Hkv * G, Hkv, 128, P, dtype, window, ds, ps)
+    _cover_check(qsl, seq, ring, plan, window)
+    c = plan.counts()
+    fast = dtype == "bf16" and P >= 8
+    if not fast:
+        assert c["decode"] == 0 and c["prefill"] == 0
+    if fast and G <= 16:
+        assert c["rowwise"] == 0
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_plan_of_workloads(idx):
+    from synth import make_workload
+    w = make_workload(idx)
+    from oracle.reference import schedule
+    s = schedule(w)
+    for l, lay in enumerate(w.layers):
+        ring = s["layers"][l]["ring_len"] if lay.ring_len > 0 else None
+        plan = cb.plan_attention(s["query_start_loc"], s["seq_lens"], ring, w.Hq, w.Hkv, w.D, w.page_size, w.dtype,
+                                 lay.window_left)
+        _cover_check(s["query_start_loc"], s["seq_lens"], ring, plan, lay.window_left)
+        assert plan.info.max_page_index < s["layers"][l]["width"]
+        if w.dtype == "f32":
+            assert plan.counts()["rowwise"] >= s["num_tokens"]
+
+
+def test_plan_rejects_bad_input():
+    with pytest.raises(cb.CbError):
+        cb.plan_attention([0, 2], [1], None, 8, 2, 128, 16, "bf16")          # seq_len < q_len
+    with pytest.raises(cb.CbError):
+        cb.plan_attention([0, 1], [5], None, 8, 3, 128, 16, "bf16")          # Hq not a multiple of Hkv
+    with pytest.raises(cb.CbError):
+        cb.plan_attention([0, 1], [5], None, 8, 2, 96, 16, "bf16")           # head_dim
+    with pytest.raises(cb.CbError):
+        cb.plan_attention([0, 1], [5], None, 8, 2, 128, 12, "bf16")          # page size
+    with pytest.raises(cb.CbError):
+        cb.plan_attention([0, 1], [5], None, 8, 2, 128, 16, "bf16", -1, 100)  # split not a multiple of 64
+    empty = cb.plan_attention([0], [], None, 8, 2, 128, 16, "bf16")
+    assert empty.info.used == 0
