@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of one mixed continuous-batching step of paged attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+
+A step is the whole hot path over one synthetic batch: host scheduling and planning into pinned memory, one
+host-to-device metadata copy, the KV append, split-KV decode, prefill tiles and the merge of split rows, for every
+layer of the workload. Steps run back to back on one stream, the host preparing step k+1 while the device runs
+step k. Inputs (caches with the history, the step's new Q/K/V rows) are resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout; progress goes to stderr. The headline workload is the mixed chunked-prefill step
+under max_batch_tokens 2048 (96 decodes, two continuing 512-token chunks and a 928-token new prompt; 32 query /
+8 kv heads, head_dim 128, bf16, page 16).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "mixed-batch paged attention: query tokens/s + KV GB/s (% HBM / % MFMA peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DEVICE_SRC = os.path.join(ROOT, "paged_kv_attention_varlen_amd", "csrc", "cb_device.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(w, sched):
+    """What the method must move or compute, per layer (no padding, no partial results).
+
+    decode kernel bytes: every visible key of a decode row read once per kv head (K and V), plus its Q and O rows.
+    prefill flops: 4*D per (query row, head, visible key) -- QK^T and PV, causal count.
+    kv bytes: every visible key of every request read once per kv head (K and V).
+    """
+    e = 2 if w.dtype == "bf16" else 4
+    qsl, seq = sched["query_start_loc"], sched["seq_lens"]
+    out = []
+    for lay in w.layers:
+        wl = lay.window_left
+        dec_bytes = pre_flops = kv_bytes = 0
+        n_dec = 0
+        for r in range(sched["num_reqs"]):
+            q = int(qsl[r + 1] - qsl[r])
+            ctx = int(seq[r]) - q
+            pos = np.arange(ctx, ctx + q)
+            lo = np.zeros_like(pos) if wl < 0 else np.maximum(0, pos - wl)
+            n_vis = pos - lo + 1
+            kv_bytes += int(ctx + q - lo[0]) * w.Hkv * 2 * w.D * e
+            if q == 1:
+                n_dec += 1
+                dec_bytes += int(n_vis[0]) * w.Hkv * 2 * w.D * e + 2 * w.Hq * w.D * e
+            else:
+                pre_flops += int(n_vis.sum()) * 4 * w.D * w.Hq
+        out.append({"decode_bytes": dec_bytes, "prefill_flops": pre_flops, "kv_bytes": kv_bytes, "decodes": n_dec})
+    return out
+
+
+def stored_traffic():
+    """HBM bytes per decode launch from a rocprofv3 counter run, if taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        sha = hashlib.sha256(open(DEVICE_SRC, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != sha:
+            return None
+        return rec.get("traffic_bytes_per_launch")
+    except Exception:  # noqa: BLE001
+        return None
+
+
+def cpu_baseline(w, sched, seconds: float):
+    """Time the oracle (as it stands) on a bounded sample of the step's query rows: all decode rows first, then
+    prefill rows drawn at random from the chunks, until `seconds` of oracle time. Input generation is not timed."""
+    from oracle import attention as A
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    qsl, seq, idx = sched["query_start_loc"], sched["seq_lens"], sched["req_index"]
+    nd = sched["num_decodes"]
+    order = [(r, 0) for r in range(nd)]
+    pre = [(r, i) for r in range(nd, sched["num_reqs"]) for i in range(int(qsl[r + 1] - qsl[r]))]
+    rng = np.random.default_rng(0)
+    order += [pre[j] for j in rng.permutation(len(pre))]
+    layer = 0
+    wl = w.layers[layer].window_left
+    done, spent = 0, 0.0
+    for r, i in order:
+        if spent >= seconds:
+            break
+        q_len = int(qsl[r + 1] - qsl[r])
+        ctx = int(seq[r]) - q_len
+        pos = ctx + i
+        lo = A.visible_range(pos, wl)[0]
+        k = w.values("k", int(idx[r]), layer, lo, pos + 1)
+        v = w.values("v", int(idx[r]), layer, lo, pos + 1)
+        qr = w.values("q", int(idx[r]), layer, pos, pos + 1)
+        t0 = time.perf_counter()
+        A.attend_rows(qr, k, v, lo, [pos], w.scale, wl)
+        spent += time.perf_counter() - t0
+        done += 1
+    return {"value": done / spent if spent > 0 else None, "unit": "query tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} query rows of layer '{w.layers[layer].name}' ({min(done, nd)} decode rows, "
+                      f"{max(0, done - nd)} prefill rows drawn at random from the chunks), fp64 numpy, "
+                      f"{spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--decode-split", type=int, default=0)
+    ap.add_argument("--prefill-split", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU "
+              "path: the step would shard by kv heads or by requests with no exchange inside attention)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_attention_varlen_amd import load_library
+    from paged_kv_attention_varlen_amd.step import Step, StepPipeline
+    from synth import make_workload
+
+    load_library()
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    w = make_workload(args.workload)
+    log(f"[bench] workload {args.workload}: {w.name}")
+    t = time.time()
+    step = Step.from_workload(w, decode_split=args.decode_split, prefill_split=args.prefill_split, threads=16)
+    pipe = StepPipeline(w, step, args.decode_split, args.prefill_split)
+    sched = step.sched
+    log(f"[bench] setup {time.time() - t:.1f}s; N={sched['num_reqs']} T={sched['num_tokens']} "
+        f"decodes={sched['num_decodes']}; plans {[L.plan.counts() for L in step.layers]}")
+
+    for _ in range(args.warmup):
+        pipe.run()
+    torch.cuda.synchronize()
+    L = len(w.layers)
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(L)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        pipe.run(events[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step")
+
+    # per-kernel durations from the events (same stream as the launches)
+    dec_ms = [[events[k][l][0].elapsed_time(events[k][l][1]) for k in range(args.steps)] for l in range(L)]
+    pre_ms = [[events[k][l][1].elapsed_time(events[k][l][2]) for k in range(args.steps)] for l in range(L)]
+    com_ms = [[events[k][l][2].elapsed_time(events[k][l][3]) for k in range(args.steps)] for l in range(L)]
+    work = algorithmic_work(w, sched)
+    T = sched["num_tokens"]
+    value = T / (ms_per_step / 1e3)
+    kv_bytes = sum(x["kv_bytes"] for x in work)
+
+    dec_t = sum(float(np.mean(dec_ms[l])) for l in range(L) if work[l]["decodes"])
+    dec_b = sum(x["decode_bytes"] for x in work)
+    roofline = None
+    if dec_t > 0:
+        achieved = dec_b / (dec_t / 1e3) / 1e9
+        roofline = {"bound": "hbm", "kernel": "decode_kernel (split-KV decode)", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": stored_traffic(), "algorithmic_bytes_per_step": dec_b,
+                    "launches_per_step": sum(1 for x in work if x["decodes"]),
+                    "avg_launch_us": round(dec_t * 1e3 / max(1, sum(1 for x in work if x["decodes"])), 2)}
+    pre_t = sum(float(np.mean(pre_ms[l])) for l in range(L))
+    pre_f = sum(x["prefill_flops"] for x in work)
+    roofline_prefill = None
+    if pre_f > 0 and pre_t > 0:
+        tf = pre_f / (pre_t / 1e3) / 1e12
+        roofline_prefill = {"bound": "mfma", "kernel": "prefill_kernel (bf16 MFMA tiles)", "achieved": round(tf, 1),
+                            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                            "algorithmic_flops_per_step": pre_f, "avg_launch_us": round(pre_t * 1e3 / L, 2)}
+
+    base = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        base = cpu_baseline(w, sched, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1) Q/K/V, shuffled page pools)",
+        "config": {"workload": w.name, "requests": sched["num_reqs"], "query_tokens": T,
+                   "decodes": sched["num_decodes"], "layers": [x.name for x in w.layers],
+                   "kv_tokens_visible": int(kv_bytes // (w.Hkv * 2 * w.D * (2 if w.dtype == "bf16" else 4)))},
+        "kv_gb_per_s": round(kv_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "kernel_us": {"decode": round(dec_t * 1e3, 2), "prefill_and_rowwise": round(pre_t * 1e3, 2),
+                      "combine": round(sum(float(np.mean(com_ms[l])) for l in range(L)) * 1e3, 2)},
+        "roofline": roofline, "roofline_prefill": roofline_prefill, "cpu_baseline": base,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,7 +22,7 @@ from ._abi import (CB_DECODING, CB_DTYPE_BF16, CB_DTYPE_F32, CB_E_CAPACITY, CB_E
                    CbError)
 
 __all__ = ["build_metadata", "plan_attention", "kv_append", "paged_attention", "workspace_size", "AttnPlan",
-           "load_library", "CbError"]
+           "Scheduler", "plan_into", "load_library", "CbError"]
 
 
 def load_library():
@@ -100,6 +100,58 @@ def build_metadata(requests, layers, max_batch_tokens: int, max_requests: int, p
                             "ring_len": buf[step.off_ring_len[l]:step.off_ring_len[l] + N].copy(),
                             "used_pages": step.used_pages[l], "width": w})
     return o
+
+
+class Scheduler:
+    """cb_build_metadata's arguments marshalled once, for repeated calls that write into caller buffers (e.g. pinned
+    host memory that is then copied to the device in one transfer)."""
+
+    def __init__(self, requests, layers, max_batch_tokens: int, max_requests: int, page_size: int,
+                 safety_margin: float = 0.0, pad_page: int = 0):
+        self._lib = _abi.load()
+        self._keep = []
+        n, L = len(requests), len(layers)
+        self.n, self.L = n, L
+        self.reqs = (_abi.cb_req * max(n, 1))()
+        for i, rq in enumerate(requests):
+            r = self.reqs[i]
+            r.id, r.state, r.num_computed, r.num_pending = int(rq.id), int(rq.state), int(rq.num_computed), \
+                int(rq.num_pending)
+            for l in range(L):
+                p = _i32(rq.pages[l])
+                self._keep.append(p)
+                r.n_pages[l] = p.size
+                r.pages[l] = _ptr(p)
+        self.pools = (_abi.cb_layer_pool * max(L, 1))()
+        for l, lay in enumerate(layers):
+            f = _i32(lay["free_pages"])
+            self._keep.append(f)
+            self.pools[l] = _abi.cb_layer_pool(int(lay["ring_len"]), int(lay["window_left"]), int(lay["pool_pages"]),
+                                               f.size, _ptr(f))
+        self.params = _abi.cb_sched_params(int(max_batch_tokens), int(max_requests), int(page_size), int(pad_page),
+                                           L, float(safety_margin))
+
+    def build_into(self, out: np.ndarray) -> _abi.cb_step:
+        """Schedule into `out` (a C-contiguous int32 array); returns the header. Raises on any status but OK."""
+        step = _abi.cb_step()
+        st = self._lib.cb_build_metadata(self.reqs, self.n, C.byref(self.params), self.pools,
+                                         out.ctypes.data_as(_abi.i32p), out.size, C.byref(step))
+        if st != CB_OK:
+            raise CbError(st, "cb_build_metadata")
+        return step
+
+
+def plan_into(query_start_loc: np.ndarray, seq_lens: np.ndarray, ring_len, shape: _abi.cb_attn_shape,
+              out: np.ndarray) -> AttnPlan:
+    """cb_plan_attention writing into `out` (C-contiguous int32 array); returns the plan with `buffer` = its view."""
+    info = _abi.cb_plan()
+    n = seq_lens.size
+    st = _abi.load().cb_plan_attention(_ptr(query_start_loc), _ptr(seq_lens), None if ring_len is None else
+                                       _ptr(ring_len), n, C.byref(shape), out.ctypes.data_as(_abi.i32p), out.size,
+                                       C.byref(info))
+    if st != CB_OK:
+        raise CbError(st, "cb_plan_attention")
+    return AttnPlan(info, shape, out[:int(info.used)])
 
 
 # ------------------------------------------------------------------------------------------- cb_plan_attention

@@ -79,6 +79,12 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m paged_kv_attention_varlen_amd.build`")
+    # torch first: the library then binds to the HIP runtime torch already loaded, so device pointers and streams
+    # from torch tensors are valid in the library's launches (one runtime per process)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = C.CDLL(path)
     lib.cb_build_metadata.restype = C.c_int32
     lib.cb_build_metadata.argtypes = [C.POINTER(cb_req), C.c_int32, C.POINTER(cb_sched_params),

@@ -114,8 +114,16 @@ __global__ __launch_bounds__(256) void kv_append_kernel(T *__restrict__ kc, T *_
 // lane l owns the scores of keys 8(l/16) .. 8(l/16)+7 for head l%16 -- exactly its B operand of the PV product --
 // and a V^T operand of 8 consecutive keys is one 16-byte load.
 
+constexpr int kDecodeMaxPages = 1040;   // page ids of one decode split staged in LDS (split / page + 2)
+
 template <int D>
-__global__ __launch_bounds__(256) void decode_kernel(const uint16_t *__restrict__ q, uint16_t *__restrict__ out,
+struct DecodeTile {
+    u32x4 k[2][D / 32];   // K rows of both 16-key halves, d = 32kb + 8(l/16) .. +8
+    u32x4 v[D / 16];      // V^T rows d = 16b + l%16, keys 8(l/16) .. +8
+};
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(const uint16_t *__restrict__ q, uint16_t *__restrict__ out,
                                                      const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
                                                      const int32_t *__restrict__ block_table, int table_width,
                                                      int num_pages, const int32_t *__restrict__ items,
@@ -126,6 +134,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t *__restrict_
     __shared__ float sm_o[4][D][17];
     __shared__ float sm_m[4][16];
     __shared__ float sm_l[4][16];
+    __shared__ int sm_page[kDecodeMaxPages];
 
     const int32_t *it = items + int64_t(blockIdx.x) * 8;
     const int r = it[0], t = it[1], kv_lo = it[3], kv_hi = it[4], slot = it[5], ring = it[6];
@@ -135,7 +144,14 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t *__restrict_
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15;   // head in the group (N index) and A row index
     const int rg = lane >> 4;    // 0..3
-    const int32_t *bt = block_table + int64_t(r) * table_width;
+
+    // the split's page ids, once, into LDS
+    const int blk0 = kv_lo >> P_log2;
+    {
+        const int32_t *bt = block_table + int64_t(r) * table_width;
+        const int nblk = ((kv_hi - 1) >> P_log2) - blk0 + 1;
+        for (int i = threadIdx.x; i < nblk; i += 256) sm_page[i] = lookup_page(bt, blk0 + i, ring, num_pages);
+    }
 
     // Q as the B operand of the QK product: head `col`, d = 32kb + 8rg .. +8
     bf16x8 qf[KB];
@@ -145,56 +161,60 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t *__restrict_
         if (col < G) v = load16(q + (int64_t(t) * Hq + g * G + col) * D + 32 * kb + 8 * rg);
         qf[kb] = as_bf16x8(v);
     }
+    __syncthreads();
 
     // K row handled by this lane in each half tile: A row `col` of half hf holds key 8(col/4) + 4hf + col%4
     const int krow0 = 8 * (col >> 2) + (col & 3);
+    const int64_t head_k = int64_t(g) * P * D;      // offset of kv head g inside a K page
+    const int64_t head_v = int64_t(g) * D * P;      // and inside a V page
+    const int64_t page_elems = int64_t(Hkv) * P * D;
 
-    float m = kNegInf, l = 0.f;
-    f32x4 acc[DB];
-#pragma unroll
-    for (int b = 0; b < DB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int tile_first = kv_lo >> 5, tile_last = (kv_hi - 1) >> 5;
-    for (int tile = tile_first + wave; tile <= tile_last; tile += 4) {
+    auto load_tile = [&](int tile, DecodeTile<D> &b) {
         const int base = tile << 5;
-        const bool edge = base < kv_lo || base + 32 > kv_hi;
-        // ---- loads: K rows for both halves, V^T columns of keys base+8rg .. +8
-        u32x4 kreg[2][KB];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int key = base + krow0 + 4 * hf;
             if (key >= kv_lo && key < kv_hi) {
-                const int page = lookup_page(bt, key >> P_log2, ring, num_pages);
-                const uint16_t *src = kc + ((int64_t(page) * Hkv + g) * P + (key & (P - 1))) * D + 8 * rg;
+                const int page = sm_page[(key >> P_log2) - blk0];
+                const uint16_t *src = kc + page * page_elems + head_k + int64_t(key & (P - 1)) * D + 8 * rg;
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) kreg[hf][kb] = load16(src + 32 * kb);
+                for (int kb = 0; kb < KB; ++kb) b.k[hf][kb] = load16(src + 32 * kb);
             } else {
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) kreg[hf][kb] = u32x4{0, 0, 0, 0};
+                for (int kb = 0; kb < KB; ++kb) b.k[hf][kb] = u32x4{0, 0, 0, 0};
             }
         }
-        u32x4 vreg[DB];
         const int key8 = base + 8 * rg;
         if (key8 + 8 > kv_lo && key8 < kv_hi) {
             const int first = key8 < kv_lo ? kv_lo : key8;   // any valid key of the group locates the page
-            const int page = lookup_page(bt, first >> P_log2, ring, num_pages);
-            const uint16_t *src = vc + ((int64_t(page) * Hkv + g) * D + col) * P + (key8 & (P - 1));
+            const int page = sm_page[(first >> P_log2) - blk0];
+            const uint16_t *src = vc + page * page_elems + head_v + int64_t(col) * P + (key8 & (P - 1));
 #pragma unroll
-            for (int b = 0; b < DB; ++b) vreg[b] = load16(src + int64_t(16 * b) * P);
-            if (edge) {
-#pragma unroll
-                for (int b = 0; b < DB; ++b) vreg[b] = mask_keys8(vreg[b], key8, kv_lo, kv_hi);
-            }
+            for (int bb = 0; bb < DB; ++bb) b.v[bb] = load16(src + int64_t(16 * bb) * P);
         } else {
 #pragma unroll
-            for (int b = 0; b < DB; ++b) vreg[b] = u32x4{0, 0, 0, 0};
+            for (int bb = 0; bb < DB; ++bb) b.v[bb] = u32x4{0, 0, 0, 0};
         }
-        // ---- scores
+    };
+
+    float m = kNegInf, l = 0.f;
+    f32x4 acc[DB];
+#pragma unroll
+    for (int bb = 0; bb < DB; ++bb) acc[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute_tile = [&](int tile, DecodeTile<D> &b) {
+        const int base = tile << 5;
+        const int key8 = base + 8 * rg;
+        const bool edge = base < kv_lo || base + 32 > kv_hi;
+        if (edge) {
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb) b.v[bb] = mask_keys8(b.v[bb], key8, kv_lo, kv_hi);
+        }
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[0][kb]), qf[kb], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[1][kb]), qf[kb], s1, 0, 0, 0);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(b.k[0][kb]), qf[kb], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(b.k[1][kb]), qf[kb], s1, 0, 0, 0);
         }
         float s[8];
 #pragma unroll
@@ -209,7 +229,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t *__restrict_
                 if (key < kv_lo || key >= kv_hi) s[e] = kNegInf;
             }
         }
-        // ---- online softmax for head `col` (its 32 keys sit in lanes col, col+16, col+32, col+48)
+        // online softmax for head `col` (its 32 keys sit in lanes col, col+16, col+32, col+48)
         float tmax = s[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, s[e]);
@@ -229,9 +249,28 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t *__restrict_
         l = l * alpha + psum;
         m = m_new;
 #pragma unroll
-        for (int b = 0; b < DB; ++b) {
-            acc[b] *= alpha;
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vreg[b]), pf, acc[b], 0, 0, 0);
+        for (int bb = 0; bb < DB; ++bb) {
+            acc[bb] *= alpha;
+            acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(b.v[bb]), pf, acc[bb], 0, 0, 0);
+        }
+    };
+
+    // tiles of 32 keys, round-robin over the 4 waves; the next tile's loads are in flight while one is computed
+    const int tile_last = (kv_hi - 1) >> 5;
+    int tile = (kv_lo >> 5) + wave;
+    if (tile <= tile_last) {
+        DecodeTile<D> ta, tb;
+        load_tile(tile, ta);
+        while (true) {
+            const int t1 = tile + 4;
+            if (t1 <= tile_last) load_tile(t1, tb);
+            compute_tile(tile, ta);
+            if (t1 > tile_last) break;
+            const int t2 = t1 + 4;
+            if (t2 <= tile_last) load_tile(t2, ta);
+            compute_tile(t1, tb);
+            if (t2 > tile_last) break;
+            tile = t2;
         }
     }
     // ---- per-wave totals, then merge the 4 waves
@@ -242,9 +281,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t *__restrict_
         sm_l[wave][col] = l;
     }
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+    for (int bb = 0; bb < DB; ++bb)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) sm_o[wave][16 * b + 4 * rg + u][col] = acc[b][u];
+        for (int u = 0; u < 4; ++u) sm_o[wave][16 * bb + 4 * rg + u][col] = acc[bb][u];
     __syncthreads();
     for (int idx = threadIdx.x; idx < G * D; idx += 256) {
         const int n = idx / D, d = idx % D;
@@ -404,32 +443,56 @@ __global__ __launch_bounds__(64) void rowwise_kernel(const T *__restrict__ q, T 
 
 constexpr int kPfRows = 128;
 constexpr int kPfKeys = 64;
+constexpr int kPrefillMaxPages = 1536;   // page ids of one prefill item staged in LDS (split / page + 2)
+constexpr float kRescaleSlack = 8.f;   // log2 units the running maximum may lag behind the true one
 
-template <int D>
-__global__ __launch_bounds__(256) void prefill_kernel(const uint16_t *__restrict__ q, uint16_t *__restrict__ out,
-                                                      const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
-                                                      const int32_t *__restrict__ block_table, int table_width,
-                                                      int num_pages, const int32_t *__restrict__ items,
-                                                      float *__restrict__ part_o, float *__restrict__ part_ml, int Hq,
-                                                      int Hkv, int P_log2, float scale_log2e, int window_left) {
-    constexpr int KB = D / 16;    // QK MFMAs per 32-key half
-    constexpr int DB = D / 32;    // output blocks of 32 d-rows
-    constexpr int KPAD = D + 8;   // LDS row pitch of K (elements)
-    constexpr int VPAD = kPfKeys + 8;
-    __shared__ uint16_t sk[kPfKeys * KPAD];
-    __shared__ uint16_t sv[D * VPAD];
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Sum of 8 bf16 values in fp32 (the same rounded weights the PV product uses).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 p, float acc) {
+    const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16x2 pr = {p[2 * i], p[2 * i + 1]};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+    }
+    return acc;
+}
+
+template <int D, int PL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
+    const uint16_t *__restrict__ q, uint16_t *__restrict__ out, const uint16_t *__restrict__ kc,
+    const uint16_t *__restrict__ vc, const int32_t *__restrict__ block_table, int table_width, int num_pages,
+    const int32_t *__restrict__ items, float *__restrict__ part_o, float *__restrict__ part_ml, int Hq, int Hkv,
+    float scale_log2e, int window_left) {
+    constexpr int P = 1 << PL;
+    constexpr int KB = D / 16;                 // QK MFMAs per 32-key half
+    constexpr int DB = D / 32;                 // output blocks of 32 d-rows
+    constexpr int KPAD = D + 8;                // LDS row pitch of K (elements)
+    constexpr int VPAD = kPfKeys + 8;          // LDS row pitch of V^T (elements)
+    constexpr int KCH = kPfKeys * D / 8 / 256; // 16-byte K chunks per thread per tile
+    constexpr int VCH = D * kPfKeys / 8 / 256; // 16-byte V^T chunks per thread per tile
+    constexpr int RUN = P < kPfKeys ? P : kPfKeys;   // keys of one page inside a tile
+    constexpr int PER_ROW = RUN / 8;                 // 16-byte chunks of one d-row of one page
+    constexpr int PPT = kPfKeys / RUN;               // pages per tile
+    __shared__ uint16_t sk[2][kPfKeys * KPAD];
+    __shared__ uint16_t sv[2][D * VPAD];
+    __shared__ int s_pages[kPrefillMaxPages];   // page id of every logical block the item touches
 
     const int32_t *it = items + int64_t(blockIdx.x) * 8;
     const int r = it[0], t0 = it[1], pos0 = it[2], qc = it[3], kv_lo = it[4], kv_hi = it[5];
     const int slot_base = it[6], ring = it[7];
     const int g = blockIdx.y;
     const int G = Hq / Hkv;
-    const int P = 1 << P_log2;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int c32 = lane & 31, half = lane >> 5;
     const int32_t *bt = block_table + int64_t(r) * table_width;
+    const int64_t page_elems = int64_t(Hkv) * P * D;
+    const uint16_t *kc_g = kc + int64_t(g) * P * D;
+    const uint16_t *vc_g = vc + int64_t(g) * D * P;
 
-    // this lane's row
+    // this lane's row (token-major: row = token * G + head)
     const int row = 32 * wave + c32;
     const int ti = row / G, hn = row % G;
     const bool row_ok = ti < qc;
@@ -437,16 +500,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint16_t *__restrict
     const int rlo = row_ok ? max(kv_lo, window_left < 0 ? 0 : pos - window_left) : 1;
     const int rhi = row_ok ? min(pos, kv_hi - 1) : 0;   // inclusive
 
-    // keys any row of the group can see
+    // keys any row of the group sees, and the ranges this wave's valid rows span
     const int ulo = max(kv_lo, window_left < 0 ? 0 : pos0 - window_left);
     const int uhi = min(kv_hi, pos0 + qc);   // exclusive
-    // keys every valid row of this wave sees (no masking needed inside)
     const int wr0 = 32 * wave, wr1 = min(32 * wave + 31, qc * G - 1);
-    int full_lo = 0x7fffffff, full_hi = -1;
+    int full_lo = 0x7fffffff, full_hi = -1, any_lo = 0x7fffffff, any_hi = -1;
     if (wr0 <= wr1) {
         const int pa = pos0 + wr0 / G, pb = pos0 + wr1 / G;
-        full_lo = max(kv_lo, window_left < 0 ? 0 : pb - window_left);
+        full_lo = max(kv_lo, window_left < 0 ? 0 : pb - window_left);   // every row sees [full_lo, full_hi]
         full_hi = min(pa, kv_hi - 1);
+        any_lo = max(kv_lo, window_left < 0 ? 0 : pa - window_left);    // some row sees [any_lo, any_hi]
+        any_hi = min(pb, kv_hi - 1);
     }
 
     bf16x8 qf[KB];
@@ -465,93 +529,146 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint16_t *__restrict
         for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
 
     const int krow_sw = ((c32 >> 3) & 1) << 2 | ((c32 >> 2) & 1) << 3 | (c32 & ~12);   // bits 2 and 3 swapped
-
     const int tile_first = ulo / kPfKeys, tile_last = (uhi - 1) / kPfKeys;
-    for (int tile = tile_first; tile <= tile_last; ++tile) {
+    const int ntiles = tile_last - tile_first + 1;
+
+    // the item's page ids, once, into LDS (blocks outside [ulo, uhi) read page 0: in bounds, masked later)
+    const int blk0 = ulo >> PL;
+    const int nblk = ((uhi - 1) >> PL) - blk0 + 1;
+    for (int i = tid; i < nblk; i += 256) s_pages[i] = lookup_page(bt, blk0 + i, ring, num_pages);
+    auto page_of_key = [&](int key) {
+        const int i = (key >> PL) - blk0;
+        return (i >= 0 && i < nblk) ? s_pages[i] : 0;
+    };
+    // chunk geometry: K chunk j covers key row kr = tid/(D/8) + (256/(D/8)) j, d = 8 (tid % (D/8));
+    // V chunk j covers page pi, d-row d, keys 8kk .. +8 of that page's run inside the tile.
+    // Loads are unconditional (invalid keys read page 0); keys outside [ulo, uhi) are zeroed when stored to LDS,
+    // so no load result is inspected before the store and the loads stay in flight through the compute.
+    u32x4 kreg[KCH], vreg[VCH];
+    auto load_tile = [&](int tile) {
         const int base = tile * kPfKeys;
-        __syncthreads();
-        // ---- stage K rows [64][D]: 16-byte chunks, a key row's chunks on consecutive threads
-        for (int c = threadIdx.x; c < kPfKeys * (D / 8); c += 256) {
-            const int kr = c / (D / 8), cc = c % (D / 8);
-            const int key = base + kr;
-            u32x4 v = {0, 0, 0, 0};
-            if (key >= ulo && key < uhi) {
-                const int page = lookup_page(bt, key >> P_log2, ring, num_pages);
-                v = load16(kc + ((int64_t(page) * Hkv + g) * P + (key & (P - 1))) * D + 8 * cc);
-            }
-            store16(&sk[kr * KPAD + 8 * cc], v);
-        }
-        // ---- stage V^T [D][64]: walk each page's d-major slice contiguously
-        {
-            const int run = P < kPfKeys ? P : kPfKeys;   // keys of one page inside the tile
-            const int per_row = run / 8;                  // 16-byte chunks per d-row of one page
-            for (int c = threadIdx.x; c < D * (kPfKeys / 8); c += 256) {
-                const int pi = c / (D * per_row);
-                const int w = c % (D * per_row);
-                const int d = w / per_row, kk = w % per_row;
-                const int kt = pi * run + 8 * kk;   // key offset inside the tile
-                const int key8 = base + kt;
-                u32x4 v = {0, 0, 0, 0};
-                if (key8 + 8 > ulo && key8 < uhi) {
-                    const int first = key8 < ulo ? ulo : key8;
-                    const int page = lookup_page(bt, first >> P_log2, ring, num_pages);
-                    v = load16(vc + ((int64_t(page) * Hkv + g) * D + d) * P + (key8 & (P - 1)));
-                    if (key8 < ulo || key8 + 8 > uhi) v = mask_keys8(v, key8, ulo, uhi);
-                }
-                store16(&sv[d * VPAD + kt], v);
-            }
-        }
-        __syncthreads();
+        const int toff = P > kPfKeys ? (base & (P - 1)) : 0;   // tile start inside its page (pages > 64 keys)
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int sbase = base + 32 * sub;
-            if (sbase >= uhi || sbase + 32 <= ulo) continue;
-            // ---- S^T = K Q^T
-            f32x16 s = {};
-            const uint16_t *ka = &sk[(32 * sub + krow_sw) * KPAD + 8 * half];
+        for (int j = 0; j < KCH; ++j) {
+            const int c = tid + 256 * j;
+            const int kr = c / (D / 8), cc = c % (D / 8);
+            const int page = page_of_key(base + kr);
+            kreg[j] = load16(kc_g + page * page_elems + int64_t(toff + (kr % RUN)) * D + 8 * cc);
+        }
+#pragma unroll
+        for (int j = 0; j < VCH; ++j) {
+            const int c = tid + 256 * j;
+            const int pi = c / (D * PER_ROW);
+            const int w = c % (D * PER_ROW);
+            const int d = w / PER_ROW, kk = w % PER_ROW;
+            const int page = page_of_key(base + pi * RUN);
+            vreg[j] = load16(vc_g + page * page_elems + int64_t(d) * P + toff + 8 * kk);
+        }
+    };
+    auto store_tile = [&](int tile, int buf) {
+        const int base = tile * kPfKeys;
+        const bool interior = base >= ulo && base + kPfKeys <= uhi;
+#pragma unroll
+        for (int j = 0; j < KCH; ++j) {
+            const int c = tid + 256 * j;
+            const int kr = c / (D / 8);
+            u32x4 v = kreg[j];
+            if (!interior && (base + kr < ulo || base + kr >= uhi)) v = u32x4{0, 0, 0, 0};
+            store16(&sk[buf][kr * KPAD + 8 * (c % (D / 8))], v);
+        }
+#pragma unroll
+        for (int j = 0; j < VCH; ++j) {
+            const int c = tid + 256 * j;
+            const int pi = c / (D * PER_ROW);
+            const int w = c % (D * PER_ROW);
+            const int kt = pi * RUN + 8 * (w % PER_ROW);
+            u32x4 v = vreg[j];
+            if (!interior) v = mask_keys8(v, base + kt, ulo, uhi);
+            store16(&sv[buf][(w / PER_ROW) * VPAD + kt], v);
+        }
+    };
+    auto softmax_pv = [&](f32x16 &sacc, int sbase, int sub, int buf) {
+        // lane's 16 scores: keys sbase + 8*half + 16*(v/8) + v%8
+        if (!(sbase >= full_lo && sbase + 31 <= full_hi)) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int key = sbase + 8 * half + 16 * (v >> 3) + (v & 7);
+                if (key < rlo || key > rhi) sacc[v] = kNegInf;
+            }
+        }
+        float tmax = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
+#pragma unroll
+        for (int v = 3; v < 15; v += 2) tmax = fmaxf(fmaxf(tmax, sacc[v]), sacc[v + 1]);
+        tmax = fmaxf(tmax, sacc[15]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2e;
+        // move the running maximum only when it would otherwise fall more than kRescaleSlack behind
+        const bool bump = tmax > m + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(bump)) {
+            const float m_new = bump ? tmax : m;
+            const float alpha = bump ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+            l *= alpha;
+#pragma unroll
+            for (int b = 0; b < DB; ++b) acc[b] *= alpha;
+            m = m_new;
+        }
+        const float m_use = m == kNegInf ? 0.f : m;
+        bf16x8 pf[2];
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            pf[v >> 3][v & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2e, -m_use)));
+        l = sum_bf16x8(pf[1], sum_bf16x8(pf[0], l));
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const uint16_t *va = &sv[buf][(32 * b + c32) * VPAD + 32 * sub + 16 * kk + 8 * half];
+                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(load16(va)), pf[kk], acc[b], 0, 0, 0);
+            }
+        }
+    };
+    auto compute_tile = [&](int tile, int buf) {
+        const int base = tile * kPfKeys;
+        // a 32-key half no row of this wave sees is skipped
+        const bool do0 = !(base > any_hi || base + 31 < any_lo);
+        const bool do1 = !(base + 32 > any_hi || base + 63 < any_lo);
+        const uint16_t *ka0 = &sk[buf][krow_sw * KPAD + 8 * half];
+        const uint16_t *ka1 = &sk[buf][(32 + krow_sw) * KPAD + 8 * half];
+        f32x16 s0 = {}, s1 = {};
+        if (do0 && do1) {
+            // two independent accumulation chains, interleaved
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(load16(ka0 + 16 * kb)), qf[kb], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(load16(ka1 + 16 * kb)), qf[kb], s1, 0, 0, 0);
+            }
+            softmax_pv(s0, base, 0, buf);
+            softmax_pv(s1, base + 32, 1, buf);
+        } else if (do0) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(load16(ka + 16 * kb)), qf[kb], s, 0, 0, 0);
-            // lane's 16 scores: keys sbase + 8*half + 16*(v/8) + v%8
-            const bool inner = sbase >= full_lo && sbase + 31 <= full_hi;
-            float sc[16];
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(load16(ka0 + 16 * kb)), qf[kb], s0, 0, 0, 0);
+            softmax_pv(s0, base, 0, buf);
+        } else if (do1) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                sc[v] = s[v] * scale_log2e;
-                if (!inner) {
-                    const int key = sbase + 8 * half + 16 * (v >> 3) + (v & 7);
-                    if (key < rlo || key > rhi) sc[v] = kNegInf;
-                }
-            }
-            float tmax = sc[0];
-#pragma unroll
-            for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, sc[v]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-            const float m_new = fmaxf(m, tmax);
-            const float m_use = m_new == kNegInf ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-            bf16x8 pf[2];
-            float psum = 0.f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float p = __builtin_amdgcn_exp2f(sc[v] - m_use);
-                psum += p;
-                pf[v >> 3][v & 7] = static_cast<__bf16>(p);
-            }
-            l = l * alpha + psum;
-            m = m_new;
-            // ---- O^T += V^T P^T
-#pragma unroll
-            for (int b = 0; b < DB; ++b) {
-                acc[b] *= alpha;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const uint16_t *va = &sv[(32 * b + c32) * VPAD + 32 * sub + 16 * kk + 8 * half];
-                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(load16(va)), pf[kk], acc[b], 0, 0, 0);
-                }
-            }
+            for (int kb = 0; kb < KB; ++kb)
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(load16(ka1 + 16 * kb)), qf[kb], s1, 0, 0, 0);
+            softmax_pv(s1, base + 32, 1, buf);
         }
+    };
+
+    // ---- pipeline: K/V of the next tile load into registers while the current tile is computed from LDS
+    __syncthreads();   // page ids visible
+    load_tile(tile_first);
+    store_tile(tile_first, 0);
+    __syncthreads();
+    for (int j = 0; j < ntiles; ++j) {
+        const int cur = j & 1;
+        if (j + 1 < ntiles) load_tile(tile_first + j + 1);
+        compute_tile(tile_first + j, cur);
+        if (j + 1 < ntiles) store_tile(tile_first + j + 1, cur ^ 1);
+        __syncthreads();
     }
+
     l += __shfl_xor(l, 32);
     if (!row_ok) return;
     const int h = g * G + hn;
@@ -591,27 +708,43 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint16_t *__restrict
 
 // =========================================================================================== merge of splits
 //
-// out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s, for each (token, head).
+// out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s, for each (token, head). One work group per
+// (merge item, head): the first wave folds the split maxima and sums, then every thread merges one d.
 
 template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(T *__restrict__ out, const float *__restrict__ part_o,
+__global__ __launch_bounds__(128) void combine_kernel(T *__restrict__ out, const float *__restrict__ part_o,
                                                       const float *__restrict__ part_ml,
                                                       const int32_t *__restrict__ items, int Hq, int D) {
+    __shared__ float s_ml[2];
     const int32_t *it = items + int64_t(blockIdx.x) * 4;
     const int t = it[0], first = it[1], n = it[2], stride = it[3];
-    for (int idx = threadIdx.x; idx < Hq * D; idx += blockDim.x) {
-        const int h = idx / D, d = idx % D;
+    const int h = blockIdx.y;
+    if (threadIdx.x < 64) {
         float M = kNegInf;
-        for (int s = 0; s < n; ++s) M = fmaxf(M, part_ml[((int64_t(first) + int64_t(s) * stride) * Hq + h) * 2]);
-        float L = 0.f, O = 0.f;
-        if (M != kNegInf) {
+        for (int s = threadIdx.x; s < n; s += 64)
+            M = fmaxf(M, part_ml[((int64_t(first) + int64_t(s) * stride) * Hq + h) * 2]);
+        M = wave_max(M);
+        float L = 0.f;
+        if (M != kNegInf)
+            for (int s = threadIdx.x; s < n; s += 64) {
+                const int64_t sl = int64_t(first) + int64_t(s) * stride;
+                L += part_ml[(sl * Hq + h) * 2 + 1] * exp2f(part_ml[(sl * Hq + h) * 2] - M);
+            }
+        L = wave_sum(L);
+        if (threadIdx.x == 0) {
+            s_ml[0] = M;
+            s_ml[1] = L;
+        }
+    }
+    __syncthreads();
+    const float M = s_ml[0], L = s_ml[1];
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        float O = 0.f;
+        if (M != kNegInf)
             for (int s = 0; s < n; ++s) {
                 const int64_t sl = int64_t(first) + int64_t(s) * stride;
-                const float f = exp2f(part_ml[(sl * Hq + h) * 2] - M);
-                L += part_ml[(sl * Hq + h) * 2 + 1] * f;
-                O += part_o[(sl * Hq + h) * D + d] * f;
+                O += part_o[(sl * Hq + h) * D + d] * exp2f(part_ml[(sl * Hq + h) * 2] - M);
             }
-        }
         out[(int64_t(t) * Hq + h) * D + d] = from_f32<T>(L > 0.f ? O / L : 0.f);
     }
 }
@@ -686,8 +819,9 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
     const int G = Hq / Hkv;
     const bool bf16 = sh.dtype == CB_DTYPE_BF16;
     if ((pl.n_decode > 0 || pl.n_prefill > 0) && (!bf16 || sh.page_size < 8)) return CB_E_INVAL;
-    if (pl.n_decode > 0 && G > 16) return CB_E_INVAL;
-    if (pl.n_prefill > 0 && (G > kPfRows || kPfRows % G != 0 || pl.prefill_tokens != kPfRows / G))
+    if (pl.n_decode > 0 && (G > 16 || pl.decode_split / sh.page_size + 2 > kDecodeMaxPages)) return CB_E_INVAL;
+    if (pl.n_prefill > 0 && (G > kPfRows || kPfRows % G != 0 || pl.prefill_tokens != kPfRows / G ||
+                             pl.prefill_split / sh.page_size + 2 > kPrefillMaxPages))
         return CB_E_INVAL;
     const size_t need = cb_paged_attention_workspace_size(a);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return CB_E_WORKSPACE;
@@ -735,22 +869,35 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
         uint16_t *oo = static_cast<uint16_t *>(a->out);
         const uint16_t *kk = static_cast<const uint16_t *>(a->k_cache);
         const uint16_t *vv = static_cast<const uint16_t *>(a->v_cache);
-        if (D == 128)
-            hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,
-                               a->table_width, a->num_pages, plan + pl.off_prefill, part_o, part_ml, Hq, Hkv, Pl,
-                               sl2e, sh.window_left);
-        else
-            hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,
-                               a->table_width, a->num_pages, plan + pl.off_prefill, part_o, part_ml, Hq, Hkv, Pl,
-                               sl2e, sh.window_left);
+#define CB_PREFILL(DD, PLOG)                                                                                   \
+    hipLaunchKernelGGL((prefill_kernel<DD, PLOG>), grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,      \
+                       a->table_width, a->num_pages, plan + pl.off_prefill, part_o, part_ml, Hq, Hkv, sl2e,    \
+                       sh.window_left)
+#define CB_PREFILL_D(DD)                                                                                       \
+    switch (Pl) {                                                                                              \
+        case 3: CB_PREFILL(DD, 3); break;                                                                      \
+        case 4: CB_PREFILL(DD, 4); break;                                                                      \
+        case 5: CB_PREFILL(DD, 5); break;                                                                      \
+        case 6: CB_PREFILL(DD, 6); break;                                                                      \
+        case 7: CB_PREFILL(DD, 7); break;                                                                      \
+        default: CB_PREFILL(DD, 8); break;                                                                     \
+    }
+        if (D == 128) {
+            CB_PREFILL_D(128)
+        } else {
+            CB_PREFILL_D(64)
+        }
+#undef CB_PREFILL_D
+#undef CB_PREFILL
     }
     if (pl.n_combine > 0 && (ph & CB_PHASE_COMBINE)) {
+        const dim3 grid(unsigned(pl.n_combine), unsigned(Hq));
         if (bf16)
-            hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(unsigned(pl.n_combine)), dim3(256), 0, s,
-                               static_cast<uint16_t *>(a->out), part_o, part_ml, plan + pl.off_combine, Hq, D);
+            hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(128), 0, s, static_cast<uint16_t *>(a->out),
+                               part_o, part_ml, plan + pl.off_combine, Hq, D);
         else
-            hipLaunchKernelGGL(combine_kernel<float>, dim3(unsigned(pl.n_combine)), dim3(256), 0, s,
-                               static_cast<float *>(a->out), part_o, part_ml, plan + pl.off_combine, Hq, D);
+            hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(128), 0, s, static_cast<float *>(a->out), part_o,
+                               part_ml, plan + pl.off_combine, Hq, D);
     }
     return hipGetLastError() == hipSuccess ? CB_OK : CB_E_HIP;
 }

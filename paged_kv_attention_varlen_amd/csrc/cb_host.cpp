@@ -255,7 +255,8 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
 
 namespace {
 
-constexpr int kPrefillRows = 128;   // query rows (token x grouped head) of one prefill tile
+constexpr int kPrefillRows = 128;       // query rows (token x grouped head) of one prefill tile
+constexpr int kPrefillMaxPages = 1536;  // page ids of one prefill item the device kernel stages in LDS
 constexpr int kNumCUs = 256;
 
 struct Item {
@@ -313,13 +314,15 @@ extern "C" cb_status cb_plan_attention(const int32_t *qsl, const int32_t *seq_le
     }
     int32_t PS = sh->prefill_split;
     if (PS == 0) {
-        const int64_t groups = std::max<int64_t>(1, n_tiles * Hkv);
-        const int64_t avg = ceil_div(tile_work, std::max<int64_t>(1, n_tiles));
-        // aim for >= 2 groups per CU; never cut below 512 keys
-        const int64_t want = std::max<int64_t>(1, ceil_div(2 * kNumCUs, groups));
-        const int64_t per = ceil_div(avg, want);
-        PS = int32_t(std::min<int64_t>(1 << 20, std::max<int64_t>(512, ceil_div(per, 64) * 64)));
+        // Split a tile's key range only as far as load balance needs: every split writes fp32 partial rows that the
+        // merge reads back. Items may be up to ~1.25x the average work of one of the ~2 work-group slots per CU.
+        const int64_t slots = 2 * kNumCUs;
+        const int64_t per_slot = ceil_div(tile_work * Hkv, slots);
+        PS = int32_t(std::min<int64_t>(1 << 20, std::max<int64_t>(512, ceil_div(per_slot * 5 / 4, 64) * 64)));
     }
+    // a prefill item's page ids are staged in LDS: at most kPrefillMaxPages - 2 pages of keys per split
+    PS = int32_t(std::min<int64_t>(PS, int64_t(kPrefillMaxPages - 2) * P / 64 * 64));
+    if (PS < 64) return CB_E_UNSUPPORTED;
 
     std::vector<Item> dec, pre, rowwise;
     std::vector<int32_t> comb;
@@ -375,6 +378,14 @@ extern "C" cb_status cb_plan_attention(const int32_t *qsl, const int32_t *seq_le
         }
     }
     if (slots > INT32_MAX / 2) return CB_E_UNSUPPORTED;
+    // heaviest items first: work groups are dispatched roughly in index order, so this packs the CUs like
+    // longest-processing-time-first scheduling and keeps long items out of the tail
+    auto by_keys = [](const Item &a, const Item &b) { return a.v[4] - a.v[3] > b.v[4] - b.v[3]; };
+    std::stable_sort(dec.begin(), dec.end(), by_keys);
+    std::stable_sort(rowwise.begin(), rowwise.end(), by_keys);
+    std::stable_sort(pre.begin(), pre.end(), [](const Item &a, const Item &b) {
+        return int64_t(a.v[5] - a.v[4]) * a.v[3] > int64_t(b.v[5] - b.v[4]) * b.v[3];
+    });
 
     std::memset(plan, 0, sizeof(*plan));
     plan->n_decode = int32_t(dec.size());

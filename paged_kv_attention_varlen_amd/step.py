@@ -188,3 +188,96 @@ def _fill_history(w, l: int, kc, vc, pool, device, dt, chunk_tokens: int = 1 << 
             if n >= chunk_tokens:
                 flush()
     flush()
+
+
+class StepPipeline:
+    """Runs a step again and again the way a serving loop would, every §8 stage included each time.
+
+    Per step: the host schedules (cb_build_metadata) and plans every layer (cb_plan_attention) straight into a
+    pinned int32 buffer, copies it to the device in one asynchronous transfer, then enqueues append and attention
+    reading the metadata from that copy. Two host/device buffer pairs alternate, so the host prepares step k+1
+    while the device still runs step k; the host only waits for the transfer of step k-1 before reusing its pinned
+    buffer. The device caches and new Q/K/V rows are the Step's.
+    """
+
+    def __init__(self, w, step: Step, decode_split: int = 0, prefill_split: int = 0):
+        from . import Scheduler, _abi
+        torch = _torch()
+        self.step = step
+        self.w = w
+        pools = [{"ring_len": lay.ring_len, "window_left": lay.window_left,
+                  "pool_pages": lay.num_pages - len(lay.padding_pages), "free_pages": lay.free_pages}
+                 for lay in w.layers]
+        pad = w.layers[0].padding_pages[0] if w.layers[0].padding_pages else 0
+        self.sched = Scheduler(w.requests, pools, w.max_batch_tokens, w.max_requests, w.page_size, w.safety_margin,
+                               pad)
+        dt = _abi.CB_DTYPE_BF16 if w.dtype == "bf16" else _abi.CB_DTYPE_F32
+        self.shapes = [_abi.cb_attn_shape(w.Hq, w.Hkv, w.D, w.page_size, dt, lay.window_left, decode_split,
+                                          prefill_split) for lay in w.layers]
+        # capacity: the one-off Step already built this schedule and these plans
+        meta = 8 * (step.sched["num_tokens"] + 4 * step.sched["num_reqs"] + 64) + sum(
+            L["block_table"].size for L in step.sched["layers"])
+        plan = sum(L.plan.buffer.size for L in step.layers)
+        self.meta_cap = int(meta)
+        self.cap = int(meta + 2 * plan + 1024)
+        self.host = [torch.empty(self.cap, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.dev = [torch.empty(self.cap, dtype=torch.int32, device=step.layers[0].out.device) for _ in range(2)]
+        self.copied = [None, None]
+        self.k = 0
+
+    def prepare(self):
+        """Host half of a step: schedule + plan into the next pinned buffer, start its transfer. Returns views."""
+        torch = _torch()
+        i = self.k % 2
+        self.k += 1
+        if self.copied[i] is not None:
+            self.copied[i].synchronize()
+        host = self.host[i].numpy()
+        hs = self.sched.build_into(host[:self.meta_cap])
+        N, T = hs.num_reqs, hs.num_tokens
+        qsl = host[hs.off_query_start_loc:hs.off_query_start_loc + N + 1]
+        seq = host[hs.off_seq_lens:hs.off_seq_lens + N]
+        at = int(hs.used)
+        plans = []
+        for l, lay in enumerate(self.w.layers):
+            ring = host[hs.off_ring_len[l]:hs.off_ring_len[l] + N] if lay.ring_len > 0 else None
+            from . import plan_into
+            p = plan_into(qsl, seq, ring, self.shapes[l], host[at:])
+            plans.append((p, at))
+            at += int(p.info.used)
+        dev = self.dev[i]
+        dev[:at].copy_(self.host[i][:at], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self.copied[i] = ev
+        views = []
+        for l in range(len(self.w.layers)):
+            w_ = hs.table_width[l]
+            bt = dev[hs.off_block_table[l]:hs.off_block_table[l] + N * w_].view(N, w_)
+            sm = dev[hs.off_slot_mapping[l]:hs.off_slot_mapping[l] + T]
+            p, off = plans[l]
+            views.append((bt, sm, p, dev[off:off + int(p.info.used)]))
+        return views
+
+    def run(self, events=None):
+        """One full step. `events`, if given, is a list of 4 torch events per layer recorded around the kernels:
+        after the append, after the decode kernel, after the prefill/per-token kernels, after the merge."""
+        st = self.step
+        views = self.prepare()
+        for l, (bt, sm, plan, pdev) in enumerate(views):
+            L = st.layers[l]
+            kv_append(L.k_cache, L.v_cache, L.k_new, L.v_new, sm)
+            ev = events[l] if events else None
+            if ev:
+                ev[0].record()
+                paged_attention(L.out, L.q, L.k_cache, L.v_cache, bt, plan, pdev, st.scale, L.workspace,
+                                phases=CB_PHASE_DECODE)
+                ev[1].record()
+                paged_attention(L.out, L.q, L.k_cache, L.v_cache, bt, plan, pdev, st.scale, L.workspace,
+                                phases=CB_PHASE_ROWWISE | CB_PHASE_PREFILL)
+                ev[2].record()
+                paged_attention(L.out, L.q, L.k_cache, L.v_cache, bt, plan, pdev, st.scale, L.workspace,
+                                phases=CB_PHASE_COMBINE)
+                ev[3].record()
+            else:
+                paged_attention(L.out, L.q, L.k_cache, L.v_cache, bt, plan, pdev, st.scale, L.workspace)
