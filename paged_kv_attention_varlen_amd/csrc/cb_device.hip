@@ -459,6 +459,19 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 p, float acc) {
     return acc;
 }
 
+// Direct global -> LDS copy of 16 bytes per lane: lane L's bytes land at lds_base + 16 L (lds_base wave-uniform).
+__device__ __forceinline__ void load_lds16(const void *src, void *lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// max of x over lanes l and l ^ 32
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int D, int PL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     const uint16_t *__restrict__ q, uint16_t *__restrict__ out, const uint16_t *__restrict__ kc,
@@ -466,18 +479,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int32_t *__restrict__ items, float *__restrict__ part_o, float *__restrict__ part_ml, int Hq, int Hkv,
     float scale_log2e, int window_left) {
     constexpr int P = 1 << PL;
-    constexpr int KB = D / 16;                 // QK MFMAs per 32-key half
-    constexpr int DB = D / 32;                 // output blocks of 32 d-rows
-    constexpr int KPAD = D + 8;                // LDS row pitch of K (elements)
-    constexpr int VPAD = kPfKeys + 8;          // LDS row pitch of V^T (elements)
-    constexpr int KCH = kPfKeys * D / 8 / 256; // 16-byte K chunks per thread per tile
-    constexpr int VCH = D * kPfKeys / 8 / 256; // 16-byte V^T chunks per thread per tile
+    constexpr int KB = D / 16;                   // QK MFMAs per 32-key half
+    constexpr int DB = D / 32;                   // output blocks of 32 d-rows
+    constexpr int KROW = D * 2;                  // bytes of one K row in LDS
+    constexpr int KSLOTS = D / 8;                // 16-byte slots per K row
+    constexpr int K_BYTES = kPfKeys * KROW;
+    constexpr int V_BYTES = D * kPfKeys * 2;     // V^T rows of 64 keys = 128 bytes
+    constexpr int BUF = K_BYTES + V_BYTES;
+    constexpr int K_LOADS = K_BYTES / 1024 / 4;  // 1 KB direct loads per wave per tile
+    constexpr int V_LOADS = V_BYTES / 1024 / 4;
     constexpr int RUN = P < kPfKeys ? P : kPfKeys;   // keys of one page inside a tile
-    constexpr int PER_ROW = RUN / 8;                 // 16-byte chunks of one d-row of one page
-    constexpr int PPT = kPfKeys / RUN;               // pages per tile
-    __shared__ uint16_t sk[2][kPfKeys * KPAD];
-    __shared__ uint16_t sv[2][D * VPAD];
-    __shared__ int s_pages[kPrefillMaxPages];   // page id of every logical block the item touches
+    // LDS tiles are unpadded; 16-byte slots are XOR-swizzled so the MFMA operand reads (16 rows at one column)
+    // hit distinct banks: K rows of 256 B use slot ^ (row % 16), rows of 128 B use slot ^ ((row / 2) % 8)
+    // two distinct LDS objects (not one array): the loads streaming into one provably do not alias the reads
+    // of the other, so the compiler does not wait for the stream before reading the current tile
+    __shared__ __attribute__((aligned(1024))) uint8_t smem0[BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem1[BUF];
+    __shared__ int s_pages[kPrefillMaxPages];
 
     const int32_t *it = items + int64_t(blockIdx.x) * 8;
     const int r = it[0], t0 = it[1], pos0 = it[2], qc = it[3], kv_lo = it[4], kv_hi = it[5];
@@ -513,6 +531,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         any_hi = min(pb, kv_hi - 1);
     }
 
+    // the item's page ids, once, into LDS
+    const int blk0 = ulo >> PL;
+    const int nblk = ((uhi - 1) >> PL) - blk0 + 1;
+    for (int i = tid; i < nblk; i += 256) s_pages[i] = lookup_page(bt, blk0 + i, ring, num_pages);
+    // keys outside the item's blocks read the nearest staged page: a real page of the pool, so the copy stays in
+    // bounds; those keys are masked (K) or zeroed (V) before use
+    auto page_of_key = [&](int key) { return s_pages[min(max((key >> PL) - blk0, 0), nblk - 1)]; };
+
     bf16x8 qf[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -528,66 +554,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
 
-    const int krow_sw = ((c32 >> 3) & 1) << 2 | ((c32 >> 2) & 1) << 3 | (c32 & ~12);   // bits 2 and 3 swapped
     const int tile_first = ulo / kPfKeys, tile_last = (uhi - 1) / kPfKeys;
     const int ntiles = tile_last - tile_first + 1;
 
-    // the item's page ids, once, into LDS (blocks outside [ulo, uhi) read page 0: in bounds, masked later)
-    const int blk0 = ulo >> PL;
-    const int nblk = ((uhi - 1) >> PL) - blk0 + 1;
-    for (int i = tid; i < nblk; i += 256) s_pages[i] = lookup_page(bt, blk0 + i, ring, num_pages);
-    auto page_of_key = [&](int key) {
-        const int i = (key >> PL) - blk0;
-        return (i >= 0 && i < nblk) ? s_pages[i] : 0;
-    };
-    // chunk geometry: K chunk j covers key row kr = tid/(D/8) + (256/(D/8)) j, d = 8 (tid % (D/8));
-    // V chunk j covers page pi, d-row d, keys 8kk .. +8 of that page's run inside the tile.
-    // Loads are unconditional (invalid keys read page 0); keys outside [ulo, uhi) are zeroed when stored to LDS,
-    // so no load result is inspected before the store and the loads stay in flight through the compute.
-    u32x4 kreg[KCH], vreg[VCH];
-    auto load_tile = [&](int tile) {
+    // ---- one tile (64 keys) of K rows and V^T columns straight from the pages into LDS buffer b
+    auto issue_tile = [&](int tile, uint8_t *kbuf) {
         const int base = tile * kPfKeys;
         const int toff = P > kPfKeys ? (base & (P - 1)) : 0;   // tile start inside its page (pages > 64 keys)
+        uint8_t *vbuf = kbuf + K_BYTES;
+        // all page lookups first (branch-free LDS reads), then the copies
+        int kpage[K_LOADS], vpage[V_LOADS];
 #pragma unroll
-        for (int j = 0; j < KCH; ++j) {
-            const int c = tid + 256 * j;
-            const int kr = c / (D / 8), cc = c % (D / 8);
-            const int page = page_of_key(base + kr);
-            kreg[j] = load16(kc_g + page * page_elems + int64_t(toff + (kr % RUN)) * D + 8 * cc);
+        for (int j = 0; j < K_LOADS; ++j) {
+            const int kr = (wave * K_LOADS + j) * (1024 / KROW) + lane / KSLOTS;
+            kpage[j] = page_of_key(base + kr);
         }
 #pragma unroll
-        for (int j = 0; j < VCH; ++j) {
-            const int c = tid + 256 * j;
-            const int pi = c / (D * PER_ROW);
-            const int w = c % (D * PER_ROW);
-            const int d = w / PER_ROW, kk = w % PER_ROW;
-            const int page = page_of_key(base + pi * RUN);
-            vreg[j] = load16(vc_g + page * page_elems + int64_t(d) * P + toff + 8 * kk);
+        for (int j = 0; j < V_LOADS; ++j) {
+            const int d = (wave * V_LOADS + j) * 8 + lane / 8;
+            vpage[j] = page_of_key(base + 8 * ((lane % 8) ^ ((d >> 1) & 7)));
+        }
+#pragma unroll
+        for (int j = 0; j < K_LOADS; ++j) {
+            const int blk = wave * K_LOADS + j;                        // 1 KB block of the K tile
+            const int kr = blk * (1024 / KROW) + lane / KSLOTS;        // key row
+            const int slot = lane % KSLOTS;
+            const int c = KSLOTS == 16 ? (slot ^ (kr & 15)) : (slot ^ ((kr >> 1) & 7));
+            load_lds16(kc_g + kpage[j] * page_elems + int64_t(toff + kr % RUN) * D + 8 * c, kbuf + blk * 1024);
+        }
+#pragma unroll
+        for (int j = 0; j < V_LOADS; ++j) {
+            const int blk = wave * V_LOADS + j;                        // 1 KB block of the V^T tile
+            const int d = blk * 8 + lane / 8;
+            const int kcn = (lane % 8) ^ ((d >> 1) & 7);              // 8-key chunk
+            load_lds16(vc_g + vpage[j] * page_elems + int64_t(d) * P + toff + (8 * kcn) % RUN, vbuf + blk * 1024);
         }
     };
-    auto store_tile = [&](int tile, int buf) {
+    // zero V^T entries of keys outside [ulo, uhi) (their pages may hold anything, NaN included)
+    auto fix_edge = [&](int tile, uint8_t *kbuf) {
         const int base = tile * kPfKeys;
-        const bool interior = base >= ulo && base + kPfKeys <= uhi;
-#pragma unroll
-        for (int j = 0; j < KCH; ++j) {
-            const int c = tid + 256 * j;
-            const int kr = c / (D / 8);
-            u32x4 v = kreg[j];
-            if (!interior && (base + kr < ulo || base + kr >= uhi)) v = u32x4{0, 0, 0, 0};
-            store16(&sk[buf][kr * KPAD + 8 * (c % (D / 8))], v);
-        }
-#pragma unroll
-        for (int j = 0; j < VCH; ++j) {
-            const int c = tid + 256 * j;
-            const int pi = c / (D * PER_ROW);
-            const int w = c % (D * PER_ROW);
-            const int kt = pi * RUN + 8 * (w % PER_ROW);
-            u32x4 v = vreg[j];
-            if (!interior) v = mask_keys8(v, base + kt, ulo, uhi);
-            store16(&sv[buf][(w / PER_ROW) * VPAD + kt], v);
+        uint8_t *vbuf = kbuf + K_BYTES;
+        for (int e = tid; e < D * 8; e += 256) {
+            const int d = e >> 3, kcn = e & 7;
+            const int key8 = base + 8 * kcn;
+            if (key8 >= ulo && key8 + 8 <= uhi) continue;
+            u32x4 *p = reinterpret_cast<u32x4 *>(vbuf + d * 128 + 16 * (kcn ^ ((d >> 1) & 7)));
+            *p = mask_keys8(*p, key8, ulo, uhi);
         }
     };
-    auto softmax_pv = [&](f32x16 &sacc, int sbase, int sub, int buf) {
+    auto is_edge = [&](int tile) { return tile * kPfKeys < ulo || tile * kPfKeys + kPfKeys > uhi; };
+
+    const int krow_sw = ((c32 >> 3) & 1) << 2 | ((c32 >> 2) & 1) << 3 | (c32 & ~12);   // bits 2 and 3 swapped
+    const int kswz = KSLOTS == 16 ? (krow_sw & 15) : ((krow_sw >> 1) & 7);
+    const int vswz = (c32 >> 1) & 7;
+
+    auto softmax_pv = [&](f32x16 &sacc, int sbase, int sub, const uint8_t *vbuf) {
+        // V operands first: they do not depend on the scores
+        u32x4 vop[DB][2];
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                vop[b][kk] = load16(vbuf + (32 * b + c32) * 128 + 16 * ((4 * sub + 2 * kk + half) ^ vswz));
         // lane's 16 scores: keys sbase + 8*half + 16*(v/8) + v%8
         if (!(sbase >= full_lo && sbase + 31 <= full_hi)) {
 #pragma unroll
@@ -599,8 +627,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         float tmax = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
 #pragma unroll
         for (int v = 3; v < 15; v += 2) tmax = fmaxf(fmaxf(tmax, sacc[v]), sacc[v + 1]);
-        tmax = fmaxf(tmax, sacc[15]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2e;
+        tmax = max_xor32(fmaxf(tmax, sacc[15])) * scale_log2e;
         // move the running maximum only when it would otherwise fall more than kRescaleSlack behind
         const bool bump = tmax > m + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(bump)) {
@@ -618,55 +645,79 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             pf[v >> 3][v & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2e, -m_use)));
         l = sum_bf16x8(pf[1], sum_bf16x8(pf[0], l));
 #pragma unroll
-        for (int b = 0; b < DB; ++b) {
+        for (int b = 0; b < DB; ++b)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const uint16_t *va = &sv[buf][(32 * b + c32) * VPAD + 32 * sub + 16 * kk + 8 * half];
-                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(load16(va)), pf[kk], acc[b], 0, 0, 0);
-            }
-        }
+            for (int kk = 0; kk < 2; ++kk)
+                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop[b][kk]), pf[kk], acc[b], 0, 0, 0);
     };
-    auto compute_tile = [&](int tile, int buf) {
+    auto compute_tile = [&](int tile, const uint8_t *kbuf) {
         const int base = tile * kPfKeys;
+        const uint8_t *vbuf = kbuf + K_BYTES;
         // a 32-key half no row of this wave sees is skipped
         const bool do0 = !(base > any_hi || base + 31 < any_lo);
         const bool do1 = !(base + 32 > any_hi || base + 63 < any_lo);
-        const uint16_t *ka0 = &sk[buf][krow_sw * KPAD + 8 * half];
-        const uint16_t *ka1 = &sk[buf][(32 + krow_sw) * KPAD + 8 * half];
+        auto kop = [&](int sub, int kb) {
+            return load16(kbuf + (32 * sub + krow_sw) * KROW + 16 * ((2 * kb + half) ^ kswz));
+        };
         f32x16 s0 = {}, s1 = {};
         if (do0 && do1) {
-            // two independent accumulation chains, interleaved
+            // both halves' QK chains interleaved, K operands read four MFMAs ahead
+            constexpr int NOPS = 2 * KB;
+            u32x4 ring[4];
+#pragma unroll
+            for (int n = 0; n < 4; ++n) ring[n] = kop(n & 1, n >> 1);
+            // scheduling fences keep each read four MFMAs ahead of its use (the default schedule sinks them)
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int n = 0; n < NOPS; ++n) {
+                const u32x4 a = ring[n & 3];
+                if (n & 1)
+                    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[n >> 1], s1, 0, 0, 0);
+                else
+                    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[n >> 1], s0, 0, 0, 0);
+                if (n + 4 < NOPS) ring[n & 3] = kop((n + 4) & 1, (n + 4) >> 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            softmax_pv(s0, base, 0, vbuf);
+            softmax_pv(s1, base + 32, 1, vbuf);
+        } else if (do0 || do1) {
+            const int sub = do0 ? 0 : 1;
+            u32x4 ring[4];
+#pragma unroll
+            for (int n = 0; n < 4; ++n) ring[n] = kop(sub, n);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(load16(ka0 + 16 * kb)), qf[kb], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(load16(ka1 + 16 * kb)), qf[kb], s1, 0, 0, 0);
+                const u32x4 a = ring[kb & 3];
+                if (kb + 4 < KB) ring[kb & 3] = kop(sub, kb + 4);
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[kb], s0, 0, 0, 0);
             }
-            softmax_pv(s0, base, 0, buf);
-            softmax_pv(s1, base + 32, 1, buf);
-        } else if (do0) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(load16(ka0 + 16 * kb)), qf[kb], s0, 0, 0, 0);
-            softmax_pv(s0, base, 0, buf);
-        } else if (do1) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(load16(ka1 + 16 * kb)), qf[kb], s1, 0, 0, 0);
-            softmax_pv(s1, base + 32, 1, buf);
+            softmax_pv(s0, base + 32 * sub, sub, vbuf);
         }
     };
 
-    // ---- pipeline: K/V of the next tile load into registers while the current tile is computed from LDS
-    __syncthreads();   // page ids visible
-    load_tile(tile_first);
-    store_tile(tile_first, 0);
-    __syncthreads();
-    for (int j = 0; j < ntiles; ++j) {
-        const int cur = j & 1;
-        if (j + 1 < ntiles) load_tile(tile_first + j + 1);
+    // ---- pipeline: tile j+1 streams into the other LDS buffer while tile j is computed (unrolled by two so
+    // each step names its buffers statically)
+    auto step = [&](int j, uint8_t *cur, uint8_t *nxt) {
+        if (j + 1 < ntiles) issue_tile(tile_first + j + 1, nxt);
         compute_tile(tile_first + j, cur);
-        if (j + 1 < ntiles) store_tile(tile_first + j + 1, cur ^ 1);
+        wait_vmem();
         __syncthreads();
+        if (j + 1 < ntiles && is_edge(tile_first + j + 1)) {
+            fix_edge(tile_first + j + 1, nxt);
+            __syncthreads();
+        }
+    };
+    __syncthreads();   // page ids visible
+    issue_tile(tile_first, smem0);
+    wait_vmem();
+    __syncthreads();
+    if (is_edge(tile_first)) {
+        fix_edge(tile_first, smem0);
+        __syncthreads();
+    }
+    for (int j = 0; j < ntiles; j += 2) {
+        step(j, smem0, smem1);
+        if (j + 1 < ntiles) step(j + 1, smem1, smem0);
     }
 
     l += __shfl_xor(l, 32);
