@@ -5,8 +5,11 @@
 
 A step is the whole hot path over one synthetic batch: host scheduling and planning into pinned memory, one
 host-to-device metadata copy, the KV append, split-KV decode, prefill tiles and the merge of split rows, for every
-layer of the workload. Steps run back to back on one stream, the host preparing step k+1 while the device runs
-step k. Inputs (caches with the history, the step's new Q/K/V rows) are resident in HBM before timing starts.
+layer of the workload. Steps run back to back on one stream, the host preparing step k+1 (into the other of two
+pinned/device buffer pairs) while the device runs step k. Per-kernel durations come from HIP events recorded on
+that stream around each kernel. --concurrent instead runs the prefill-tile kernels on a second stream beside the
+decode kernel (their event intervals then overlap). Inputs (caches with the history, the step's new Q/K/V rows)
+are resident in HBM before timing starts.
 
 Prints ONE JSON line on stdout; progress goes to stderr. The headline workload is the mixed chunked-prefill step
 under max_batch_tokens 2048 (96 decodes, two continuing 512-token chunks and a 928-token new prompt; 32 query /
@@ -130,6 +133,11 @@ def main():
     ap.add_argument("--prefill-split", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--concurrent", action="store_true",
+                    help="run the prefill kernels on a second stream concurrently with the decode kernel")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the steps, run a plain device copy of this many MiB three times (untimed), the "
+                         "known-size reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU "
@@ -146,11 +154,19 @@ def main():
     if not torch.cuda.is_available():
         log("no GPU visible")
         sys.exit(1)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = make_workload(args.workload)
     log(f"[bench] workload {args.workload}: {w.name}")
     t = time.time()
     step = Step.from_workload(w, decode_split=args.decode_split, prefill_split=args.prefill_split, threads=16)
-    pipe = StepPipeline(w, step, args.decode_split, args.prefill_split)
+    pipe = StepPipeline(w, step, args.decode_split, args.prefill_split, concurrent=args.concurrent)
     sched = step.sched
     log(f"[bench] setup {time.time() - t:.1f}s; N={sched['num_reqs']} T={sched['num_tokens']} "
         f"decodes={sched['num_decodes']}; plans {[L.plan.counts() for L in step.layers]}")
@@ -159,7 +175,7 @@ def main():
         pipe.run()
     torch.cuda.synchronize()
     L = len(w.layers)
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(L)] for _ in range(args.steps)]
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -171,8 +187,8 @@ def main():
 
     # per-kernel durations from the events (same stream as the launches)
     dec_ms = [[events[k][l][0].elapsed_time(events[k][l][1]) for k in range(args.steps)] for l in range(L)]
-    pre_ms = [[events[k][l][1].elapsed_time(events[k][l][2]) for k in range(args.steps)] for l in range(L)]
-    com_ms = [[events[k][l][2].elapsed_time(events[k][l][3]) for k in range(args.steps)] for l in range(L)]
+    pre_ms = [[events[k][l][2].elapsed_time(events[k][l][3]) for k in range(args.steps)] for l in range(L)]
+    com_ms = [[events[k][l][4].elapsed_time(events[k][l][5]) for k in range(args.steps)] for l in range(L)]
     work = algorithmic_work(w, sched)
     T = sched["num_tokens"]
     value = T / (ms_per_step / 1e3)

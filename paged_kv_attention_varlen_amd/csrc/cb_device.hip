@@ -28,6 +28,10 @@ constexpr float kNegInf = -INFINITY;
 
 __device__ __forceinline__ u32x4 load16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void store16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+// streaming load (non-temporal hint): for data read exactly once, such as the K/V pages of a decode split
+__device__ __forceinline__ u32x4 load16_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -71,33 +75,63 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // ============================================================================================== KV append
 //
-// One thread per (token, kv head, 16-byte chunk of the row). K chunks are copied whole; the matching V elements
-// are scattered into their d-rows at the token's page offset.
+// One work group per (group of 8 consecutive tokens of the step, kv head). K rows are copied in 16-byte chunks.
+// V goes into d-major pages: when the 8 tokens fill 8 consecutive, 8-aligned offsets of one page -- the usual case
+// inside a prefill chunk -- each d-row receives one 16-byte run (two for fp32); otherwise each element is written
+// on its own. Tokens whose slot is negative or outside the pool are skipped.
+
+constexpr int kAppendGroup = 8;
 
 template <typename T>
-__global__ __launch_bounds__(256) void kv_append_kernel(T *__restrict__ kc, T *__restrict__ vc,
+__global__ __launch_bounds__(128) void kv_append_kernel(T *__restrict__ kc, T *__restrict__ vc,
                                                         const T *__restrict__ kn, const T *__restrict__ vn,
                                                         const int32_t *__restrict__ slots, int num_tokens,
                                                         int num_pages, int P, int Hkv, int D) {
-    constexpr int E = 16 / sizeof(T);
-    const int chunks = D / E;
-    const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (gid >= int64_t(num_tokens) * Hkv * chunks) return;
-    const int c = int(gid % chunks);
-    const int64_t rest = gid / chunks;
-    const int g = int(rest % Hkv);
-    const int64_t t = rest / Hkv;
-    const int64_t slot = slots[t];
-    if (slot < 0 || slot >= int64_t(num_pages) * P) return;
-    const int64_t page = slot / P;
-    const int off = int(slot % P);
-    const int64_t src = (t * Hkv + g) * D + int64_t(c) * E;
-    store16(kc + ((page * Hkv + g) * P + off) * D + int64_t(c) * E, load16(kn + src));
-    const u32x4 v = load16(vn + src);
-    const T *ve = reinterpret_cast<const T *>(&v);
-    T *vrow = vc + ((page * Hkv + g) * D + int64_t(c) * E) * P + off;
+    constexpr int E = 16 / sizeof(T);   // elements per 16 bytes
+    constexpr int TG = kAppendGroup;
+    __shared__ int64_t s_slot[TG];
+    const int g = blockIdx.y;
+    const int64_t t0 = int64_t(blockIdx.x) * TG;
+    const int nt = int(min(int64_t(TG), int64_t(num_tokens) - t0));
+    const int64_t pool = int64_t(num_pages) * P;
+    if (threadIdx.x < TG) {
+        int64_t sl = threadIdx.x < nt ? int64_t(slots[t0 + threadIdx.x]) : -1;
+        s_slot[threadIdx.x] = (sl >= 0 && sl < pool) ? sl : -1;
+    }
+    __syncthreads();
+    const int cpr = D / E;   // 16-byte chunks per row
+    for (int c = threadIdx.x; c < nt * cpr; c += blockDim.x) {
+        const int i = c / cpr, cc = c % cpr;
+        const int64_t slot = s_slot[i];
+        if (slot < 0) continue;
+        const int64_t page = slot / P;
+        const int off = int(slot % P);
+        store16(kc + ((page * Hkv + g) * P + off) * D + int64_t(cc) * E,
+                load16(kn + ((t0 + i) * Hkv + g) * D + int64_t(cc) * E));
+    }
+    const int64_t s0 = s_slot[0];
+    bool run = nt == TG && s0 >= 0 && (s0 % P) % TG == 0 && (s0 % P) + TG <= P;
 #pragma unroll
-    for (int e = 0; e < E; ++e) vrow[int64_t(e) * P] = ve[e];
+    for (int i = 1; i < TG; ++i) run = run && s_slot[i] == s0 + i;
+    if (run) {
+        const int64_t page = s0 / P;
+        const int off = int(s0 % P);
+        for (int d = threadIdx.x; d < D; d += blockDim.x) {
+            T vals[TG];
+#pragma unroll
+            for (int i = 0; i < TG; ++i) vals[i] = vn[((t0 + i) * Hkv + g) * D + d];
+            T *dst = vc + ((page * Hkv + g) * D + d) * P + off;
+#pragma unroll
+            for (int q = 0; q < TG / E; ++q) store16(dst + q * E, *reinterpret_cast<const u32x4 *>(vals + q * E));
+        }
+    } else {
+        for (int c = threadIdx.x; c < nt * D; c += blockDim.x) {
+            const int i = c / D, d = c % D;
+            const int64_t slot = s_slot[i];
+            if (slot < 0) continue;
+            vc[((slot / P * Hkv + g) * D + d) * P + slot % P] = vn[((t0 + i) * Hkv + g) * D + d];
+        }
+    }
 }
 
 // ===================================================================== split-KV decode (bf16, MFMA 16x16x32)
@@ -178,7 +212,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const int page = sm_page[(key >> P_log2) - blk0];
                 const uint16_t *src = kc + page * page_elems + head_k + int64_t(key & (P - 1)) * D + 8 * rg;
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) b.k[hf][kb] = load16(src + 32 * kb);
+                for (int kb = 0; kb < KB; ++kb) b.k[hf][kb] = load16_stream(src + 32 * kb);
             } else {
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) b.k[hf][kb] = u32x4{0, 0, 0, 0};
@@ -190,7 +224,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int page = sm_page[(first >> P_log2) - blk0];
             const uint16_t *src = vc + page * page_elems + head_v + int64_t(col) * P + (key8 & (P - 1));
 #pragma unroll
-            for (int bb = 0; bb < DB; ++bb) b.v[bb] = load16(src + int64_t(16 * bb) * P);
+            for (int bb = 0; bb < DB; ++bb) b.v[bb] = load16_stream(src + int64_t(16 * bb) * P);
         } else {
 #pragma unroll
             for (int bb = 0; bb < DB; ++bb) b.v[bb] = u32x4{0, 0, 0, 0};
@@ -760,44 +794,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // =========================================================================================== merge of splits
 //
 // out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s, for each (token, head). One work group per
-// (merge item, head): the first wave folds the split maxima and sums, then every thread merges one d.
+// (merged token, group of 256 / (D/4) heads): each thread owns (head, 4 consecutive d), so the split maxima and sums
+// it needs and its 16-byte partial rows are independent loads that all go out at once.
 
 template <typename T>
-__global__ __launch_bounds__(128) void combine_kernel(T *__restrict__ out, const float *__restrict__ part_o,
+__global__ __launch_bounds__(256) void combine_kernel(T *__restrict__ out, const float *__restrict__ part_o,
                                                       const float *__restrict__ part_ml,
                                                       const int32_t *__restrict__ items, int Hq, int D) {
-    __shared__ float s_ml[2];
     const int32_t *it = items + int64_t(blockIdx.x) * 4;
     const int t = it[0], first = it[1], n = it[2], stride = it[3];
-    const int h = blockIdx.y;
-    if (threadIdx.x < 64) {
-        float M = kNegInf;
-        for (int s = threadIdx.x; s < n; s += 64)
-            M = fmaxf(M, part_ml[((int64_t(first) + int64_t(s) * stride) * Hq + h) * 2]);
-        M = wave_max(M);
-        float L = 0.f;
-        if (M != kNegInf)
-            for (int s = threadIdx.x; s < n; s += 64) {
-                const int64_t sl = int64_t(first) + int64_t(s) * stride;
-                L += part_ml[(sl * Hq + h) * 2 + 1] * exp2f(part_ml[(sl * Hq + h) * 2] - M);
-            }
-        L = wave_sum(L);
-        if (threadIdx.x == 0) {
-            s_ml[0] = M;
-            s_ml[1] = L;
+    const int quads = D / 4;
+    const int h = blockIdx.y * (256 / quads) + threadIdx.x / quads;
+    const int d = 4 * (threadIdx.x % quads);
+    if (h >= Hq) return;
+    float M = kNegInf;
+    for (int s = 0; s < n; ++s) M = fmaxf(M, part_ml[((int64_t(first) + int64_t(s) * stride) * Hq + h) * 2]);
+    float L = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    if (M != kNegInf) {
+        for (int s = 0; s < n; ++s) {
+            const int64_t sl = int64_t(first) + int64_t(s) * stride;
+            const float f = exp2f(part_ml[(sl * Hq + h) * 2] - M);
+            L += part_ml[(sl * Hq + h) * 2 + 1] * f;
+            O += *reinterpret_cast<const f32x4 *>(part_o + (sl * Hq + h) * D + d) * f;
         }
     }
-    __syncthreads();
-    const float M = s_ml[0], L = s_ml[1];
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        float O = 0.f;
-        if (M != kNegInf)
-            for (int s = 0; s < n; ++s) {
-                const int64_t sl = int64_t(first) + int64_t(s) * stride;
-                O += part_o[(sl * Hq + h) * D + d] * exp2f(part_ml[(sl * Hq + h) * 2] - M);
-            }
-        out[(int64_t(t) * Hq + h) * D + d] = from_f32<T>(L > 0.f ? O / L : 0.f);
-    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    T *o = out + (int64_t(t) * Hq + h) * D + d;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(O[e] * inv);
 }
 
 inline int ilog2(int x) {
@@ -829,17 +854,17 @@ extern "C" cb_status cb_kv_append(void *k_cache, void *v_cache, const void *k_ne
     if ((head_dim * esz) % 16 != 0) return CB_E_UNSUPPORTED;
     if (num_tokens == 0) return CB_OK;
     if (!k_cache || !v_cache || !k_new || !v_new || !d_slot_mapping) return CB_E_INVAL;
-    const int64_t threads = int64_t(num_tokens) * num_kv_heads * (head_dim * esz / 16);
-    const int64_t blocks = (threads + 255) / 256;
-    if (blocks > INT32_MAX) return CB_E_UNSUPPORTED;
+    const int64_t groups = (int64_t(num_tokens) + kAppendGroup - 1) / kAppendGroup;
+    if (groups > INT32_MAX || num_kv_heads > 65535) return CB_E_UNSUPPORTED;
+    const dim3 grid{static_cast<unsigned>(groups), static_cast<unsigned>(num_kv_heads), 1u};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == CB_DTYPE_F32) {
-        hipLaunchKernelGGL(kv_append_kernel<float>, dim3(unsigned(blocks)), dim3(256), 0, s,
+        hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(128), 0, s,
                            static_cast<float *>(k_cache), static_cast<float *>(v_cache),
                            static_cast<const float *>(k_new), static_cast<const float *>(v_new), d_slot_mapping,
                            num_tokens, num_pages, page_size, num_kv_heads, head_dim);
     } else {
-        hipLaunchKernelGGL(kv_append_kernel<uint16_t>, dim3(unsigned(blocks)), dim3(256), 0, s,
+        hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(128), 0, s,
                            static_cast<uint16_t *>(k_cache), static_cast<uint16_t *>(v_cache),
                            static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new),
                            d_slot_mapping, num_tokens, num_pages, page_size, num_kv_heads, head_dim);
@@ -942,12 +967,13 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
 #undef CB_PREFILL
     }
     if (pl.n_combine > 0 && (ph & CB_PHASE_COMBINE)) {
-        const dim3 grid(unsigned(pl.n_combine), unsigned(Hq));
+        const int heads_per_group = 256 / (D / 4);
+        const dim3 grid(unsigned(pl.n_combine), unsigned((Hq + heads_per_group - 1) / heads_per_group));
         if (bf16)
-            hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(128), 0, s, static_cast<uint16_t *>(a->out),
+            hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s, static_cast<uint16_t *>(a->out),
                                part_o, part_ml, plan + pl.off_combine, Hq, D);
         else
-            hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(128), 0, s, static_cast<float *>(a->out), part_o,
+            hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, static_cast<float *>(a->out), part_o,
                                part_ml, plan + pl.off_combine, Hq, D);
     }
     return hipGetLastError() == hipSuccess ? CB_OK : CB_E_HIP;

@@ -191,20 +191,25 @@ def _fill_history(w, l: int, kc, vc, pool, device, dt, chunk_tokens: int = 1 << 
 
 
 class StepPipeline:
-    """Runs a step again and again the way a serving loop would, every §8 stage included each time.
+    """Runs a step again and again the way a serving loop would, every stage included each time.
 
     Per step: the host schedules (cb_build_metadata) and plans every layer (cb_plan_attention) straight into a
-    pinned int32 buffer, copies it to the device in one asynchronous transfer, then enqueues append and attention
-    reading the metadata from that copy. Two host/device buffer pairs alternate, so the host prepares step k+1
-    while the device still runs step k; the host only waits for the transfer of step k-1 before reusing its pinned
-    buffer. The device caches and new Q/K/V rows are the Step's.
+    pinned int32 buffer, which one asynchronous copy moves to the device; two host/device buffer pairs alternate,
+    so the host prepares step k+1 while the device still runs step k (the double-buffered async batching of the
+    Transformers "continuous batching architecture" page). Then, in stream order: the KV append of every layer,
+    the split-KV decode kernel, the prefill-tile and per-token kernels, and the merge of split rows.
+
+    concurrent=True runs the prefill-tile and per-token kernels on a second compute stream beside the decode kernel
+    (decode streams HBM while prefill keeps the matrix cores busy) and joins both before the merge. All streams
+    have the default priority.
     """
 
-    def __init__(self, w, step: Step, decode_split: int = 0, prefill_split: int = 0):
+    def __init__(self, w, step: Step, decode_split: int = 0, prefill_split: int = 0, concurrent: bool = False):
         from . import Scheduler, _abi
         torch = _torch()
         self.step = step
         self.w = w
+        self.concurrent = concurrent
         pools = [{"ring_len": lay.ring_len, "window_left": lay.window_left,
                   "pool_pages": lay.num_pages - len(lay.padding_pages), "free_pages": lay.free_pages}
                  for lay in w.layers]
@@ -220,14 +225,22 @@ class StepPipeline:
         plan = sum(L.plan.buffer.size for L in step.layers)
         self.meta_cap = int(meta)
         self.cap = int(meta + 2 * plan + 1024)
+        dev = step.layers[0].out.device
         self.host = [torch.empty(self.cap, dtype=torch.int32, pin_memory=True) for _ in range(2)]
-        self.dev = [torch.empty(self.cap, dtype=torch.int32, device=step.layers[0].out.device) for _ in range(2)]
-        self.copied = [None, None]
+        self.dev = [torch.empty(self.cap, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.main = torch.cuda.current_stream(dev)
+        self.aux = torch.cuda.Stream(dev) if concurrent else None
+        self.copied = [None, None]      # copy of buffer pair i finished (host may rewrite its pinned half)
+        self.fork = torch.cuda.Event()
+        self.join = torch.cuda.Event()
         self.k = 0
 
     def prepare(self):
-        """Host half of a step: schedule + plan into the next pinned buffer, start its transfer. Returns views."""
+        """Host half of a step: schedule + plan into the next pinned buffer and enqueue its copy to the device on
+        the compute stream (stream order keeps it after the previous step's kernels that read that buffer).
+        Returns the per-layer device views."""
         torch = _torch()
+        from . import plan_into
         i = self.k % 2
         self.k += 1
         if self.copied[i] is not None:
@@ -241,14 +254,13 @@ class StepPipeline:
         plans = []
         for l, lay in enumerate(self.w.layers):
             ring = host[hs.off_ring_len[l]:hs.off_ring_len[l] + N] if lay.ring_len > 0 else None
-            from . import plan_into
             p = plan_into(qsl, seq, ring, self.shapes[l], host[at:])
             plans.append((p, at))
             at += int(p.info.used)
         dev = self.dev[i]
         dev[:at].copy_(self.host[i][:at], non_blocking=True)
         ev = torch.cuda.Event()
-        ev.record()
+        ev.record(self.main)
         self.copied[i] = ev
         views = []
         for l in range(len(self.w.layers)):
@@ -260,24 +272,41 @@ class StepPipeline:
         return views
 
     def run(self, events=None):
-        """One full step. `events`, if given, is a list of 4 torch events per layer recorded around the kernels:
-        after the append, after the decode kernel, after the prefill/per-token kernels, after the merge."""
+        """One full step. `events`, if given, holds per layer 6 timing events: decode start/end (compute stream),
+        prefill start/end (the stream running the prefill-tile and per-token kernels), merge start/end."""
         st = self.step
         views = self.prepare()
+        main = self.main
         for l, (bt, sm, plan, pdev) in enumerate(views):
             L = st.layers[l]
             kv_append(L.k_cache, L.v_cache, L.k_new, L.v_new, sm)
-            ev = events[l] if events else None
-            if ev:
-                ev[0].record()
-                paged_attention(L.out, L.q, L.k_cache, L.v_cache, bt, plan, pdev, st.scale, L.workspace,
-                                phases=CB_PHASE_DECODE)
-                ev[1].record()
-                paged_attention(L.out, L.q, L.k_cache, L.v_cache, bt, plan, pdev, st.scale, L.workspace,
-                                phases=CB_PHASE_ROWWISE | CB_PHASE_PREFILL)
-                ev[2].record()
-                paged_attention(L.out, L.q, L.k_cache, L.v_cache, bt, plan, pdev, st.scale, L.workspace,
-                                phases=CB_PHASE_COMBINE)
-                ev[3].record()
-            else:
-                paged_attention(L.out, L.q, L.k_cache, L.v_cache, bt, plan, pdev, st.scale, L.workspace)
+
+        def attend(l, phases, ev0=None, ev1=None, stream=None):
+            bt, sm, plan, pdev = views[l]
+            L = st.layers[l]
+            s = stream or main
+            if ev0 is not None:
+                ev0.record(s)
+            paged_attention(L.out, L.q, L.k_cache, L.v_cache, bt, plan, pdev, st.scale, L.workspace, stream=s,
+                            phases=phases)
+            if ev1 is not None:
+                ev1.record(s)
+
+        n = len(views)
+        E = (lambda l, k: events[l][k]) if events else (lambda l, k: None)
+        pre = CB_PHASE_ROWWISE | CB_PHASE_PREFILL
+        if self.concurrent:
+            self.fork.record(main)
+            self.aux.wait_event(self.fork)
+            for l in range(n):
+                attend(l, pre, E(l, 2), E(l, 3), self.aux)
+            for l in range(n):
+                attend(l, CB_PHASE_DECODE, E(l, 0), E(l, 1))
+            self.join.record(self.aux)
+            main.wait_event(self.join)
+        else:
+            for l in range(n):
+                attend(l, CB_PHASE_DECODE, E(l, 0), E(l, 1))
+                attend(l, pre, E(l, 2), E(l, 3))
+        for l in range(n):
+            attend(l, CB_PHASE_COMBINE, E(l, 4), E(l, 5))
