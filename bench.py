@@ -154,13 +154,21 @@ def main():
     if not torch.cuda.is_available():
         log("no GPU visible")
         sys.exit(1)
+    copy_ref = None
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
+        dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         for _ in range(3):
             dst.copy_(src)
+        e1.record()
         torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 3
+        copy_ref = {"bytes_read_plus_written": 2 * n * 4, "us": round(ms * 1e3, 1),
+                    "gb_per_s": round(2 * n * 4 / (ms / 1e3) / 1e9, 1)}
         del src, dst
     w = make_workload(args.workload)
     log(f"[bench] workload {args.workload}: {w.name}")
@@ -230,6 +238,8 @@ def main():
                       "combine": round(sum(float(np.mean(com_ms[l])) for l in range(L)) * 1e3, 2)},
         "roofline": roofline, "roofline_prefill": roofline_prefill, "cpu_baseline": base,
     }
+    if copy_ref:
+        line["device_copy_reference"] = copy_ref
     print(json.dumps(line), flush=True)
 
 
