@@ -18,8 +18,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcb.so")
 ARCH = "gfx950"
 
-# packed-fp32 VALU instructions are disabled for all device code
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# packed-fp32 VALU instructions are disabled for all device code. MFMA results are kept in ordinary VGPRs: the
+# attention kernels read every score tile back with VALU instructions, and accumulation registers would cost a copy
+# per element.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc():

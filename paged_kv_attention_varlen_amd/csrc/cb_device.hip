@@ -49,6 +49,33 @@ __device__ __forceinline__ int lookup_page(const int32_t *bt_row, int logical, i
     return p < 0 ? 0 : (p >= num_pages ? num_pages - 1 : p);
 }
 
+// Work groups are dispatched to the 8 XCDs round-robin by linear block index, and each XCD has its own L2. The work
+// groups of one kv head read the same K/V pages, so they are placed on the same XCD: linear block L runs on XCD L % 8
+// and is given a (work item, kv head) pair whose head belongs to that XCD. Returns false for the padding blocks of
+// the grid (grid size from xcd_grid).
+constexpr int kXcds = 8;
+__host__ __device__ inline int xcd_grid(int n_items, int n_heads) {
+    if (n_heads % kXcds == 0 || kXcds % n_heads != 0) return n_items * n_heads;
+    const int r = kXcds / n_heads;   // XCDs sharing one head
+    return (n_items + r - 1) / r * kXcds;
+}
+__device__ __forceinline__ bool xcd_item(int L, int n_items, int n_heads, int &item, int &head) {
+    const int x = L % kXcds, j = L / kXcds;
+    if (n_heads % kXcds == 0) {
+        const int per = n_heads / kXcds;   // heads per XCD
+        item = j / per;
+        head = x + kXcds * (j % per);
+    } else if (kXcds % n_heads == 0) {
+        const int r = kXcds / n_heads;
+        head = x % n_heads;
+        item = j * r + x / n_heads;
+    } else {
+        item = L % n_items;
+        head = L / n_items;
+    }
+    return item < n_items;
+}
+
 // Zero the bf16 elements of an 8-wide group whose key (key0 + e) lies outside [lo, hi).
 __device__ __forceinline__ u32x4 mask_keys8(u32x4 v, int key0, int lo, int hi) {
 #pragma unroll
@@ -465,20 +492,34 @@ __global__ __launch_bounds__(64) void rowwise_kernel(const T *__restrict__ q, T 
 
 // ======================================================================= prefill tiles (bf16, MFMA 32x32x16)
 //
-// Work group = one (tile of query tokens x the G heads of a kv head = 128 rows, KV range, kv head). Rows are
-// token-major (row = token * G + head). Each wave owns 32 rows. For each 64-key tile the whole group stages K rows
-// and V^T columns in LDS (coalesced page reads), then per 32-key half each wave computes
-//   S^T[key][row] = K[key][:] . Q[row][:]         D/16 MFMAs; A = K rows (from LDS), B = Q^T (registers)
-//   O^T[d][row]  += V^T[d][key] . P^T[key][row]   2 x D/32 MFMAs; A = V^T (from LDS), B = P^T (registers)
+// Work group = one (tile of query tokens x the G heads of a kv head = 128 rows, KV range, kv head); rows are
+// token-major (row = token * G + head) and each of the 4 waves owns 32 of them. Two work groups share a CU (two waves
+// per SIMD), so one's softmax arithmetic runs beside the other's matrix work. Per 64-key tile and wave:
+//   S^T[key][row] = K[key][:] . Q[row][:]         A = K rows (LDS), B = Q^T (registers)   2 halves x D/16 MFMAs
+//   O^T[d][row]  += V^T[d][key] . P^T[key][row]   A = V^T (LDS), B = P^T (registers)      4 k-steps x D/32 MFMAs
 // MFMA 32x32x16 bf16 operands: lane l holds A[l%32][8(l/32) .. +8] and B[8(l/32) .. +8][l%32]; the result gives lane l
-// column l%32 and rows 8(v/4) + 4(l/32) + v%4 for v = 0..15. Keys are fed to the QK product in an order with bits 2
-// and 3 of the index swapped, so that lane l's 16 scores are keys 8(l/32) + 16kk + 0..7 (kk = 0, 1): each group of
-// 8 is one B operand of the PV product, and the matching V^T operand is 8 consecutive keys of one d-row.
+// column l%32 and rows 8(v/4) + 4(l/32) + v%4 for v = 0..15. The K rows of a 32-key half are fed with bits 2 and 3 of
+// the key index swapped, so that lane l's 16 scores are keys 8(l/32) + 16kk + 0..7 (kk = 0, 1): each group of 8 is
+// one B operand of the PV product.
+//
+// LDS holds the K and V^T tiles in 1 KB blocks. Each block is filled by one direct global->LDS copy (lane L's 16 bytes
+// land at offset 16 L) and read back with 16-byte reads at offset 16 l, so fills and reads are linear and
+// conflict-free, and each copy reads one page (pages of >= 16 keys: the page id is wave-uniform and the address is
+// scalar; with 8-key pages a copy spans two):
+//   K block (half s, k-step pair p, key quarter qq): slot 32 kbp + 16 h + j = K[32s + 16qq + j][16(2p + kbp) + 8h ..]
+//   V block (k-step kk, d block b):                 slot 32 h + i          = V^T[32b + i][16kk + 8h ..]
+// Wave w copies key quarter w (keys 16w .. 16w + 15 of the tile: its K blocks and V k-step w).
+//
+// Per tile, with the next tile's copies in flight (double buffering):
+//   QK(half 0) | QK(half 1) beside softmax(half 0) | PV(half 0) beside softmax(half 1) | PV(half 1)
+// Softmax in the log2 domain with a lazily moved running maximum: the weights are computed speculatively against the
+// current maximum, and only when some row's tile maximum exceeds it by more than kRescaleSlack does a rare path move
+// it, rescale that row's accumulators and recompute the weights. Tiles every row sees completely skip the mask.
 
-constexpr int kPfRows = 128;
-constexpr int kPfKeys = 64;
+constexpr int kPfRows = 128;   // query rows of one work group: 4 waves x 32
+constexpr int kPfKeys = 64;    // keys per tile
 constexpr int kPrefillMaxPages = 1536;   // page ids of one prefill item staged in LDS (split / page + 2)
-constexpr float kRescaleSlack = 8.f;   // log2 units the running maximum may lag behind the true one
+constexpr float kRescaleSlack = 8.f;     // log2 units the running maximum may lag behind the true one
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -510,76 +551,60 @@ template <int D, int PL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     const uint16_t *__restrict__ q, uint16_t *__restrict__ out, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ block_table, int table_width, int num_pages,
-    const int32_t *__restrict__ items, float *__restrict__ part_o, float *__restrict__ part_ml, int Hq, int Hkv,
-    float scale_log2e, int window_left) {
+    const int32_t *__restrict__ items, int n_items, float *__restrict__ part_o, float *__restrict__ part_ml, int Hq,
+    int Hkv, float scale_log2e, int window_left) {
     constexpr int P = 1 << PL;
-    constexpr int KB = D / 16;                   // QK MFMAs per 32-key half
-    constexpr int DB = D / 32;                   // output blocks of 32 d-rows
-    constexpr int KROW = D * 2;                  // bytes of one K row in LDS
-    constexpr int KSLOTS = D / 8;                // 16-byte slots per K row
-    constexpr int K_BYTES = kPfKeys * KROW;
-    constexpr int V_BYTES = D * kPfKeys * 2;     // V^T rows of 64 keys = 128 bytes
-    constexpr int BUF = K_BYTES + V_BYTES;
-    constexpr int K_LOADS = K_BYTES / 1024 / 4;  // 1 KB direct loads per wave per tile
-    constexpr int V_LOADS = V_BYTES / 1024 / 4;
-    constexpr int RUN = P < kPfKeys ? P : kPfKeys;   // keys of one page inside a tile
-    // LDS tiles are unpadded; 16-byte slots are XOR-swizzled so the MFMA operand reads (16 rows at one column)
-    // hit distinct banks: K rows of 256 B use slot ^ (row % 16), rows of 128 B use slot ^ ((row / 2) % 8)
-    // two distinct LDS objects (not one array): the loads streaming into one provably do not alias the reads
-    // of the other, so the compiler does not wait for the stream before reading the current tile
-    __shared__ __attribute__((aligned(1024))) uint8_t smem0[BUF];
-    __shared__ __attribute__((aligned(1024))) uint8_t smem1[BUF];
+    constexpr int KB = D / 16;          // k-steps of the QK product
+    constexpr int DB = D / 32;          // 32-row d blocks of the output
+    constexpr int NK = KB / 2;          // K blocks per key quarter (copies per wave per tile)
+    constexpr int KT = 2 * KB * 1024;   // one K tile (64 keys)
+    constexpr int VT = 4 * DB * 1024;   // one V tile (64 keys)
+    // distinct LDS objects per buffer: the copies streaming into one provably do not alias reads of the other, so
+    // the compiler does not wait for them before reading
+    __shared__ __attribute__((aligned(1024))) uint8_t s_k0[KT];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_k1[KT];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_v0[VT];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_v1[VT];
     __shared__ int s_pages[kPrefillMaxPages];
 
-    const int32_t *it = items + int64_t(blockIdx.x) * 8;
+    int item, g;
+    if (!xcd_item(blockIdx.x, n_items, Hkv, item, g)) return;
+    const int32_t *it = items + int64_t(item) * 8;
     const int r = it[0], t0 = it[1], pos0 = it[2], qc = it[3], kv_lo = it[4], kv_hi = it[5];
     const int slot_base = it[6], ring = it[7];
-    const int g = blockIdx.y;
     const int G = Hq / Hkv;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int c32 = lane & 31, half = lane >> 5;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c32 = lane & 31, h = lane >> 5;
     const int32_t *bt = block_table + int64_t(r) * table_width;
     const int64_t page_elems = int64_t(Hkv) * P * D;
     const uint16_t *kc_g = kc + int64_t(g) * P * D;
     const uint16_t *vc_g = vc + int64_t(g) * D * P;
+    auto lo_of = [&](int p) { return window_left < 0 ? 0 : max(0, p - window_left); };
 
-    // this lane's row (token-major: row = token * G + head)
-    const int row = 32 * wave + c32;
-    const int ti = row / G, hn = row % G;
-    const bool row_ok = ti < qc;
-    const int pos = pos0 + ti;
-    const int rlo = row_ok ? max(kv_lo, window_left < 0 ? 0 : pos - window_left) : 1;
-    const int rhi = row_ok ? min(pos, kv_hi - 1) : 0;   // inclusive
+    // this lane's row and the keys it sees; a row that sees nothing gets an empty range
+    const int row = 32 * w + c32;
+    const int ti = row / G, hn = row - ti * G;
+    const bool ok = ti < qc;
+    int rlo, rspan;
+    {
+        const int pos = pos0 + ti;
+        const int lo = max(kv_lo, lo_of(pos)), hi = min(pos, kv_hi - 1);
+        const bool none = !ok || hi < lo;
+        rlo = none ? 0x7fffffff : lo;
+        rspan = none ? 0 : hi - lo;
+    }
 
-    // keys any row of the group sees, and the ranges this wave's valid rows span
-    const int ulo = max(kv_lo, window_left < 0 ? 0 : pos0 - window_left);
+    // keys any row of the group sees; tiles every row sees completely need no mask
+    const int ulo = max(kv_lo, lo_of(pos0));
     const int uhi = min(kv_hi, pos0 + qc);   // exclusive
-    const int wr0 = 32 * wave, wr1 = min(32 * wave + 31, qc * G - 1);
-    int full_lo = 0x7fffffff, full_hi = -1, any_lo = 0x7fffffff, any_hi = -1;
-    if (wr0 <= wr1) {
-        const int pa = pos0 + wr0 / G, pb = pos0 + wr1 / G;
-        full_lo = max(kv_lo, window_left < 0 ? 0 : pb - window_left);   // every row sees [full_lo, full_hi]
-        full_hi = min(pa, kv_hi - 1);
-        any_lo = max(kv_lo, window_left < 0 ? 0 : pa - window_left);    // some row sees [any_lo, any_hi]
-        any_hi = min(pb, kv_hi - 1);
-    }
-
-    // the item's page ids, once, into LDS
-    const int blk0 = ulo >> PL;
-    const int nblk = ((uhi - 1) >> PL) - blk0 + 1;
-    for (int i = tid; i < nblk; i += 256) s_pages[i] = lookup_page(bt, blk0 + i, ring, num_pages);
-    // keys outside the item's blocks read the nearest staged page: a real page of the pool, so the copy stays in
-    // bounds; those keys are masked (K) or zeroed (V) before use
-    auto page_of_key = [&](int key) { return s_pages[min(max((key >> PL) - blk0, 0), nblk - 1)]; };
-
-    bf16x8 qf[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        u32x4 v = {0, 0, 0, 0};
-        if (row_ok) v = load16(q + (int64_t(t0 + ti) * Hq + g * G + hn) * D + 16 * kb + 8 * half);
-        qf[kb] = as_bf16x8(v);
-    }
+    const int lo_max = max(kv_lo, lo_of(pos0 + qc - 1));
+    const int hi_min = min(pos0, kv_hi - 1);
+    const int tile_first = ulo / kPfKeys;
+    const int ntiles = uhi > ulo ? (uhi - 1) / kPfKeys - tile_first + 1 : 0;
+    auto clean = [&](int tile) { return tile * kPfKeys >= lo_max && tile * kPfKeys + kPfKeys - 1 <= hi_min; };
+    auto needs_vfix = [&](int tile) { return tile * kPfKeys < ulo || tile * kPfKeys + kPfKeys > uhi; };
 
     float m = kNegInf, l = 0.f;
     f32x16 acc[DB];
@@ -588,205 +613,228 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
 
-    const int tile_first = ulo / kPfKeys, tile_last = (uhi - 1) / kPfKeys;
-    const int ntiles = tile_last - tile_first + 1;
+    if (ntiles > 0) {
+        // ---- the item's page ids into LDS
+        const int blk0 = ulo >> PL;
+        const int nblk = ((uhi - 1) >> PL) - blk0 + 1;
+        for (int i = tid; i < nblk; i += 256) s_pages[i] = lookup_page(bt, blk0 + i, ring, num_pages);
+        // keys outside the item's blocks read the nearest staged page: a real page of the pool, so the copy stays in
+        // bounds; those keys are masked (K) or zeroed (V) before use
+        auto page_at = [&](int key) { return s_pages[min(max((key >> PL) - blk0, 0), nblk - 1)]; };
 
-    // ---- one tile (64 keys) of K rows and V^T columns straight from the pages into LDS buffer b
-    auto issue_tile = [&](int tile, uint8_t *kbuf) {
-        const int base = tile * kPfKeys;
-        const int toff = P > kPfKeys ? (base & (P - 1)) : 0;   // tile start inside its page (pages > 64 keys)
-        uint8_t *vbuf = kbuf + K_BYTES;
-        // all page lookups first (branch-free LDS reads), then the copies
-        int kpage[K_LOADS], vpage[V_LOADS];
-#pragma unroll
-        for (int j = 0; j < K_LOADS; ++j) {
-            const int kr = (wave * K_LOADS + j) * (1024 / KROW) + lane / KSLOTS;
-            kpage[j] = page_of_key(base + kr);
-        }
-#pragma unroll
-        for (int j = 0; j < V_LOADS; ++j) {
-            const int d = (wave * V_LOADS + j) * 8 + lane / 8;
-            vpage[j] = page_of_key(base + 8 * ((lane % 8) ^ ((d >> 1) & 7)));
-        }
-#pragma unroll
-        for (int j = 0; j < K_LOADS; ++j) {
-            const int blk = wave * K_LOADS + j;                        // 1 KB block of the K tile
-            const int kr = blk * (1024 / KROW) + lane / KSLOTS;        // key row
-            const int slot = lane % KSLOTS;
-            const int c = KSLOTS == 16 ? (slot ^ (kr & 15)) : (slot ^ ((kr >> 1) & 7));
-            load_lds16(kc_g + kpage[j] * page_elems + int64_t(toff + kr % RUN) * D + 8 * c, kbuf + blk * 1024);
-        }
-#pragma unroll
-        for (int j = 0; j < V_LOADS; ++j) {
-            const int blk = wave * V_LOADS + j;                        // 1 KB block of the V^T tile
-            const int d = blk * 8 + lane / 8;
-            const int kcn = (lane % 8) ^ ((d >> 1) & 7);              // 8-key chunk
-            load_lds16(vc_g + vpage[j] * page_elems + int64_t(d) * P + toff + (8 * kcn) % RUN, vbuf + blk * 1024);
-        }
-    };
-    // zero V^T entries of keys outside [ulo, uhi) (their pages may hold anything, NaN included)
-    auto fix_edge = [&](int tile, uint8_t *kbuf) {
-        const int base = tile * kPfKeys;
-        uint8_t *vbuf = kbuf + K_BYTES;
-        for (int e = tid; e < D * 8; e += 256) {
-            const int d = e >> 3, kcn = e & 7;
-            const int key8 = base + 8 * kcn;
-            if (key8 >= ulo && key8 + 8 <= uhi) continue;
-            u32x4 *p = reinterpret_cast<u32x4 *>(vbuf + d * 128 + 16 * (kcn ^ ((d >> 1) & 7)));
-            *p = mask_keys8(*p, key8, ulo, uhi);
-        }
-    };
-    auto is_edge = [&](int tile) { return tile * kPfKeys < ulo || tile * kPfKeys + kPfKeys > uhi; };
-
-    const int krow_sw = ((c32 >> 3) & 1) << 2 | ((c32 >> 2) & 1) << 3 | (c32 & ~12);   // bits 2 and 3 swapped
-    const int kswz = KSLOTS == 16 ? (krow_sw & 15) : ((krow_sw >> 1) & 7);
-    const int vswz = (c32 >> 1) & 7;
-
-    auto softmax_pv = [&](f32x16 &sacc, int sbase, int sub, const uint8_t *vbuf) {
-        // V operands first: they do not depend on the scores
-        u32x4 vop[DB][2];
-#pragma unroll
-        for (int b = 0; b < DB; ++b)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                vop[b][kk] = load16(vbuf + (32 * b + c32) * 128 + 16 * ((4 * sub + 2 * kk + half) ^ vswz));
-        // lane's 16 scores: keys sbase + 8*half + 16*(v/8) + v%8
-        if (!(sbase >= full_lo && sbase + 31 <= full_hi)) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = sbase + 8 * half + 16 * (v >> 3) + (v & 7);
-                if (key < rlo || key > rhi) sacc[v] = kNegInf;
+        // ---- copies of one tile into LDS: wave w copies key quarter w
+        const int k_cp = (lane & (P >= 16 ? 15 : 7)) * D + 16 * (lane >> 5) + 8 * ((lane >> 4) & 1);
+        const int v_cp = (lane & 31) * P + (P >= 16 ? 8 * (lane >> 5) : 0);
+        auto issue_k = [&](int tile, uint8_t *kbuf) {
+            const int key0 = tile * kPfKeys + 16 * w;
+            uint8_t *dst = kbuf + ((w >> 1) * NK * 2 + (w & 1)) * 1024;
+            const uint16_t *src;
+            if constexpr (P >= 16) {
+                const int pg = __builtin_amdgcn_readfirstlane(page_at(key0));
+                src = kc_g + int64_t(pg) * page_elems + (key0 & (P - 1)) * D + k_cp;
+            } else {
+                const int pg = page_at(key0 + 8 * ((lane >> 3) & 1));
+                src = kc_g + int64_t(pg) * page_elems + k_cp;
             }
-        }
-        float tmax = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
 #pragma unroll
-        for (int v = 3; v < 15; v += 2) tmax = fmaxf(fmaxf(tmax, sacc[v]), sacc[v + 1]);
-        tmax = max_xor32(fmaxf(tmax, sacc[15])) * scale_log2e;
-        // move the running maximum only when it would otherwise fall more than kRescaleSlack behind
-        const bool bump = tmax > m + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(bump)) {
-            const float m_new = bump ? tmax : m;
-            const float alpha = bump ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
-            l *= alpha;
-#pragma unroll
-            for (int b = 0; b < DB; ++b) acc[b] *= alpha;
-            m = m_new;
-        }
-        const float m_use = m == kNegInf ? 0.f : m;
-        bf16x8 pf[2];
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-            pf[v >> 3][v & 7] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2e, -m_use)));
-        l = sum_bf16x8(pf[1], sum_bf16x8(pf[0], l));
-#pragma unroll
-        for (int b = 0; b < DB; ++b)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop[b][kk]), pf[kk], acc[b], 0, 0, 0);
-    };
-    auto compute_tile = [&](int tile, const uint8_t *kbuf) {
-        const int base = tile * kPfKeys;
-        const uint8_t *vbuf = kbuf + K_BYTES;
-        // a 32-key half no row of this wave sees is skipped
-        const bool do0 = !(base > any_hi || base + 31 < any_lo);
-        const bool do1 = !(base + 32 > any_hi || base + 63 < any_lo);
-        auto kop = [&](int sub, int kb) {
-            return load16(kbuf + (32 * sub + krow_sw) * KROW + 16 * ((2 * kb + half) ^ kswz));
+            for (int p = 0; p < NK; ++p) load_lds16(src + 32 * p, dst + p * 2048);
         };
-        f32x16 s0 = {}, s1 = {};
-        if (do0 && do1) {
-            // both halves' QK chains interleaved, K operands read four MFMAs ahead
-            constexpr int NOPS = 2 * KB;
-            u32x4 ring[4];
-#pragma unroll
-            for (int n = 0; n < 4; ++n) ring[n] = kop(n & 1, n >> 1);
-            // scheduling fences keep each read four MFMAs ahead of its use (the default schedule sinks them)
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int n = 0; n < NOPS; ++n) {
-                const u32x4 a = ring[n & 3];
-                if (n & 1)
-                    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[n >> 1], s1, 0, 0, 0);
-                else
-                    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[n >> 1], s0, 0, 0, 0);
-                if (n + 4 < NOPS) ring[n & 3] = kop((n + 4) & 1, (n + 4) >> 1);
-                __builtin_amdgcn_sched_barrier(0);
+        auto issue_v = [&](int tile, uint8_t *vbuf) {
+            const int key0 = tile * kPfKeys + 16 * w;
+            uint8_t *dst = vbuf + w * DB * 1024;
+            const uint16_t *src;
+            if constexpr (P >= 16) {
+                const int pg = __builtin_amdgcn_readfirstlane(page_at(key0));
+                src = vc_g + int64_t(pg) * page_elems + (key0 & (P - 1)) + v_cp;
+            } else {
+                const int pg = page_at(key0 + 8 * h);
+                src = vc_g + int64_t(pg) * page_elems + v_cp;
             }
-            softmax_pv(s0, base, 0, vbuf);
-            softmax_pv(s1, base + 32, 1, vbuf);
-        } else if (do0 || do1) {
-            const int sub = do0 ? 0 : 1;
-            u32x4 ring[4];
 #pragma unroll
-            for (int n = 0; n < 4; ++n) ring[n] = kop(sub, n);
+            for (int b = 0; b < DB; ++b) load_lds16(src + 32 * b * P, dst + b * 1024);
+        };
+        // zero V^T entries of keys outside [ulo, uhi) (their pages may hold anything, NaN included)
+        auto fix_v = [&](int tile, uint8_t *vbuf) {
+            for (int e = tid; e < 4 * DB * 64; e += 256) {
+                const int key8 = tile * kPfKeys + 16 * ((e >> 6) / DB) + 8 * ((e >> 5) & 1);
+                if (key8 >= ulo && key8 + 8 <= uhi) continue;
+                u32x4 *p = reinterpret_cast<u32x4 *>(vbuf + e * 16);
+                *p = mask_keys8(*p, key8, ulo, uhi);
+            }
+        };
+
+        // ---- compute pieces
+        const int krow = (((c32 >> 3) & 1) << 2) | (((c32 >> 2) & 1) << 3) | (c32 & ~12);   // bits 2, 3 swapped
+        const int k_rd = (c32 >> 4) * 1024 + (16 * h + (krow & 15)) * 16;
+        // this lane's Q row as B operands of the QK product: Q[row][16kb + 8h .. +8]
+        bf16x8 qf[KB];
+        {
+            const uint16_t *qrow = q + (int64_t(t0 + ti) * Hq + g * G + hn) * D + 8 * h;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const u32x4 a = ring[kb & 3];
-                if (kb + 4 < KB) ring[kb & 3] = kop(sub, kb + 4);
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[kb], s0, 0, 0, 0);
+                u32x4 v = {0, 0, 0, 0};
+                if (ok) v = load16(qrow + 16 * kb);
+                qf[kb] = as_bf16x8(v);
             }
-            softmax_pv(s0, base + 32 * sub, sub, vbuf);
         }
-    };
+        // S^T of one 32-key half
+        auto qk_half = [&](const uint8_t *kbuf, int s, f32x16 &S) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) S[v] = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const bf16x8 a = as_bf16x8(load16(kbuf + k_rd + (s * NK + kb / 2) * 2048 + (kb & 1) * 512));
+                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], S, 0, 0, 0);
+            }
+        };
+        // O^T += V^T P^T over one 32-key half (k-steps 2s, 2s+1)
+        auto pv_half = [&](const uint8_t *vbuf, int s, const bf16x8 (&pf)[2]) {
+            const uint8_t *v_rd = vbuf + lane * 16;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int b = 0; b < DB; ++b) {
+                    const bf16x8 a = as_bf16x8(load16(v_rd + ((2 * s + kk) * DB + b) * 1024));
+                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], acc[b], 0, 0, 0);
+                }
+        };
+        // scores of keys the row does not see -> -inf (tiles on the causal diagonal or at the window's edge)
+        auto mask_half = [&](f32x16 &S, int key_base) {
+            const int base = key_base + 8 * h - rlo;
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                if (unsigned(base + 16 * (v >> 3) + (v & 7)) > unsigned(rspan)) S[v] = kNegInf;
+        };
+        auto weights = [&](const f32x16 &S, float mu, bf16x8 (&pf)[2]) {
+            float sum = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                bf16x8 p;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    p[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(S[8 * kk + e], scale_log2e, -mu)));
+                pf[kk] = p;
+                sum = sum_bf16x8(p, sum);
+            }
+            return sum;
+        };
+        // Softmax of one half against the current running maximum (speculative): the row maximum, the bf16 weights
+        // (the B operands of the PV product) and their sum. Returns whether the running maximum must move.
+        auto softmax_half = [&](const f32x16 &S, bf16x8 (&pf)[2], float &lsum, float &tmax) {
+            float x = fmaxf(S[0], S[1]);
+#pragma unroll
+            for (int v = 2; v < 16; ++v) x = fmaxf(x, S[v]);
+            tmax = max_xor32(x) * scale_log2e;
+            lsum = weights(S, m == kNegInf ? 0.f : m, pf);
+            // pin the speculative results here, beside the matrix work of this region: otherwise the compiler sinks
+            // them past the rare-path branch that follows and they no longer overlap the MFMAs
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                u32x4 t = __builtin_bit_cast(u32x4, pf[kk]);
+                asm volatile("" : "+v"(t));
+                pf[kk] = as_bf16x8(t);
+            }
+            asm volatile("" : "+v"(lsum));
+            return tmax > m + kRescaleSlack;
+        };
+        // Rare path: some row's maximum moved by more than the slack. Move it, rescale the row's accumulators and
+        // recompute its weights.
+        auto settle = [&](bool bump, const f32x16 &S, bf16x8 (&pf)[2], float &lsum, float tmax) {
+            // a loop of at most one trip rather than a branch, so that the compiler keeps the rescale out of line
+            const int trips = __builtin_amdgcn_ballot_w64(bump) ? 1 : 0;
+#pragma nounroll
+            for (int t = 0; t < trips; ++t) {
+                const float m_new = bump ? tmax : m;
+                const float alpha = bump ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+                l *= alpha;
+#pragma unroll
+                for (int b = 0; b < DB; ++b) acc[b] *= alpha;
+                m = m_new;
+                lsum = weights(S, m_new == kNegInf ? 0.f : m_new, pf);
+            }
+            l += lsum;
+        };
 
-    // ---- pipeline: tile j+1 streams into the other LDS buffer while tile j is computed (unrolled by two so
-    // each step names its buffers statically)
-    auto step = [&](int j, uint8_t *cur, uint8_t *nxt) {
-        if (j + 1 < ntiles) issue_tile(tile_first + j + 1, nxt);
-        compute_tile(tile_first + j, cur);
+        // One tile from (kcur, vcur); the next tile's copies go to (knxt, vnxt).
+        auto tile = [&](int j, const uint8_t *kcur, const uint8_t *vcur, uint8_t *knxt, uint8_t *vnxt) {
+            const int tile = tile_first + j;
+            const bool more = j + 1 < ntiles;
+            const bool edge = !clean(tile);
+            if (more) {
+                issue_k(tile + 1, knxt);
+                issue_v(tile + 1, vnxt);
+            }
+            f32x16 S0, S1;
+            bf16x8 p0[2], p1[2];
+            float ls0, ls1, tm0, tm1;
+            qk_half(kcur, 0, S0);
+            if (edge) mask_half(S0, tile * kPfKeys);
+            qk_half(kcur, 1, S1);
+            const bool b0 = softmax_half(S0, p0, ls0, tm0);
+            settle(b0, S0, p0, ls0, tm0);
+            if (edge) mask_half(S1, tile * kPfKeys + 32);
+            pv_half(vcur, 0, p0);
+            const bool b1 = softmax_half(S1, p1, ls1, tm1);
+            settle(b1, S1, p1, ls1, tm1);
+            pv_half(vcur, 1, p1);
+            // the next tile has landed for every wave; every wave is done with this one
+            wait_vmem();
+            __syncthreads();
+            if (more && needs_vfix(tile + 1)) {
+                fix_v(tile + 1, vnxt);
+                __syncthreads();
+            }
+        };
+
+        // ---- the first tile into LDS, then the tiles (buffers named statically: the loop is unrolled by two)
+        __syncthreads();   // page ids
+        issue_k(tile_first, s_k0);
+        issue_v(tile_first, s_v0);
         wait_vmem();
         __syncthreads();
-        if (j + 1 < ntiles && is_edge(tile_first + j + 1)) {
-            fix_edge(tile_first + j + 1, nxt);
+        if (needs_vfix(tile_first)) {
+            fix_v(tile_first, s_v0);
             __syncthreads();
         }
-    };
-    __syncthreads();   // page ids visible
-    issue_tile(tile_first, smem0);
-    wait_vmem();
-    __syncthreads();
-    if (is_edge(tile_first)) {
-        fix_edge(tile_first, smem0);
-        __syncthreads();
-    }
-    for (int j = 0; j < ntiles; j += 2) {
-        step(j, smem0, smem1);
-        if (j + 1 < ntiles) step(j + 1, smem1, smem0);
+        for (int j = 0; j < ntiles; j += 2) {
+            tile(j, s_k0, s_v0, s_k1, s_v1);
+            if (j + 1 < ntiles) tile(j + 1, s_k1, s_v1, s_k0, s_v0);
+        }
     }
 
+    // ---- results: lane holds O^T[d][row] for d = 32b + 8(v/4) + 4h + v%4
     l += __shfl_xor(l, 32);
-    if (!row_ok) return;
-    const int h = g * G + hn;
+    if (!ok) return;
+    const int hh = g * G + hn;
     const int tok = t0 + ti;
-    // lane holds O^T[d][row] for d = 32b + 8(v/4) + 4*half + v%4
     if (slot_base < 0) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t *orow = out + (int64_t(tok) * Hq + h) * D;
+        uint16_t *orow = out + (int64_t(tok) * Hq + hh) * D;
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
-                const int d = 32 * b + 8 * v4 + 4 * half;
-                uint32_t lo2 = uint32_t(f32_to_bf16(acc[b][4 * v4 + 0] * inv)) |
-                               uint32_t(f32_to_bf16(acc[b][4 * v4 + 1] * inv)) << 16;
-                uint32_t hi2 = uint32_t(f32_to_bf16(acc[b][4 * v4 + 2] * inv)) |
-                               uint32_t(f32_to_bf16(acc[b][4 * v4 + 3] * inv)) << 16;
+                const int d = 32 * b + 8 * v4 + 4 * h;
+                const uint32_t lo2 = uint32_t(f32_to_bf16(acc[b][4 * v4 + 0] * inv)) |
+                                     uint32_t(f32_to_bf16(acc[b][4 * v4 + 1] * inv)) << 16;
+                const uint32_t hi2 = uint32_t(f32_to_bf16(acc[b][4 * v4 + 2] * inv)) |
+                                     uint32_t(f32_to_bf16(acc[b][4 * v4 + 3] * inv)) << 16;
                 *reinterpret_cast<uint2 *>(orow + d) = make_uint2(lo2, hi2);
             }
     } else {
         const int64_t sl = int64_t(slot_base) + ti;
-        float *po = part_o + (sl * Hq + h) * D;
+        float *po = part_o + (sl * Hq + hh) * D;
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
-                const int d = 32 * b + 8 * v4 + 4 * half;
+                const int d = 32 * b + 8 * v4 + 4 * h;
                 *reinterpret_cast<f32x4 *>(po + d) =
                     f32x4{acc[b][4 * v4 + 0], acc[b][4 * v4 + 1], acc[b][4 * v4 + 2], acc[b][4 * v4 + 3]};
             }
-        if (half == 0) {
-            part_ml[(sl * Hq + h) * 2 + 0] = m;
-            part_ml[(sl * Hq + h) * 2 + 1] = l;
+        if (h == 0) {
+            part_ml[(sl * Hq + hh) * 2 + 0] = m;
+            part_ml[(sl * Hq + hh) * 2 + 1] = l;
         }
     }
 }
@@ -940,15 +988,15 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
 #undef CB_ROWWISE
     }
     if (pl.n_prefill > 0 && (ph & CB_PHASE_PREFILL)) {
-        const dim3 grid(unsigned(pl.n_prefill), unsigned(Hkv));
+        const dim3 grid(unsigned(xcd_grid(pl.n_prefill, Hkv)));
         const uint16_t *qq = static_cast<const uint16_t *>(a->q);
         uint16_t *oo = static_cast<uint16_t *>(a->out);
         const uint16_t *kk = static_cast<const uint16_t *>(a->k_cache);
         const uint16_t *vv = static_cast<const uint16_t *>(a->v_cache);
 #define CB_PREFILL(DD, PLOG)                                                                                   \
     hipLaunchKernelGGL((prefill_kernel<DD, PLOG>), grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,      \
-                       a->table_width, a->num_pages, plan + pl.off_prefill, part_o, part_ml, Hq, Hkv, sl2e,    \
-                       sh.window_left)
+                       a->table_width, a->num_pages, plan + pl.off_prefill, pl.n_prefill, part_o, part_ml, Hq, \
+                       Hkv, sl2e, sh.window_left)
 #define CB_PREFILL_D(DD)                                                                                       \
     switch (Pl) {                                                                                              \
         case 3: CB_PREFILL(DD, 3); break;                                                                      \
