@@ -138,6 +138,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--concurrent", action="store_true",
                     help="run the prefill kernels on a second stream concurrently with the decode kernel")
+    ap.add_argument("--no-copy-stream", action="store_true",
+                    help="copy each step's metadata on the compute stream instead of a stream of its own (which lets "
+                         "the copy overlap the previous step's kernels)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, run a plain device copy of this many MiB three times (untimed), the "
                          "known-size reference for scaling HBM byte counters")
@@ -177,7 +180,8 @@ def main():
     log(f"[bench] workload {args.workload}: {w.name}")
     t = time.time()
     step = Step.from_workload(w, decode_split=args.decode_split, prefill_split=args.prefill_split, threads=16)
-    pipe = StepPipeline(w, step, args.decode_split, args.prefill_split, concurrent=args.concurrent)
+    pipe = StepPipeline(w, step, args.decode_split, args.prefill_split, concurrent=args.concurrent,
+                        copy_stream=not args.no_copy_stream)
     sched = step.sched
     log(f"[bench] setup {time.time() - t:.1f}s; N={sched['num_reqs']} T={sched['num_tokens']} "
         f"decodes={sched['num_decodes']}; plans {[L.plan.counts() for L in step.layers]}")

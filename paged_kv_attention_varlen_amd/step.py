@@ -11,14 +11,15 @@ slots stay NaN.
 """
 from __future__ import annotations
 
+import ctypes as C
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import List, Optional
 
 import numpy as np
 
-from . import (CB_PHASE_COMBINE, CB_PHASE_DECODE, CB_PHASE_PREFILL, CB_PHASE_ROWWISE, AttnPlan, build_metadata,
-               kv_append, paged_attention, plan_attention, workspace_size)
+from . import (CB_PHASE_COMBINE, CB_PHASE_DECODE, CB_PHASE_PREFILL, CB_PHASE_ROWWISE, AttnPlan, CbError, _abi,
+               build_metadata, kv_append, paged_attention, plan_attention, workspace_size)
 
 
 def _torch():
@@ -200,12 +201,14 @@ class StepPipeline:
     the split-KV decode kernel, the prefill-tile and per-token kernels, and the merge of split rows.
 
     concurrent=True runs the prefill-tile and per-token kernels on a second compute stream beside the decode kernel
-    (decode streams HBM while prefill keeps the matrix cores busy) and joins both before the merge. All streams
-    have the default priority.
+    (decode streams HBM while prefill keeps the matrix cores busy) and joins both before the merge. copy_stream=True
+    moves the metadata copy to a stream of its own, so that it overlaps the previous step's kernels instead of
+    sitting between steps. All streams have the default priority.
     """
 
-    def __init__(self, w, step: Step, decode_split: int = 0, prefill_split: int = 0, concurrent: bool = False):
-        from . import Scheduler, _abi
+    def __init__(self, w, step: Step, decode_split: int = 0, prefill_split: int = 0, concurrent: bool = False,
+                 copy_stream: bool = True):
+        from . import Scheduler
         torch = _torch()
         self.step = step
         self.w = w
@@ -230,10 +233,35 @@ class StepPipeline:
         self.dev = [torch.empty(self.cap, dtype=torch.int32, device=dev) for _ in range(2)]
         self.main = torch.cuda.current_stream(dev)
         self.aux = torch.cuda.Stream(dev) if concurrent else None
-        self.copied = [None, None]      # copy of buffer pair i finished (host may rewrite its pinned half)
+        self.copier = torch.cuda.Stream(dev) if copy_stream else None
+        # events are created once (torch creates the HIP event at its first record) and re-recorded every step
+        self.copy_ev = [torch.cuda.Event(), torch.cuda.Event()]   # copy into buffer pair i finished
+        self.rel_ev = [torch.cuda.Event(), torch.cuda.Event()]    # last kernels reading device buffer i finished
         self.fork = torch.cuda.Event()
         self.join = torch.cuda.Event()
+        for e in (*self.copy_ev, *self.rel_ev, self.fork, self.join):
+            e.record(self.main)
+        self.copied = [None, None]
+        self.released = [None, None]
         self.k = 0
+        # launch arguments marshalled once: only the per-step metadata pointers change between steps
+        self.lib = _abi.load()
+        self.h_main = C.c_void_p(self.main.cuda_stream)
+        self.h_aux = C.c_void_p(self.aux.cuda_stream) if self.aux is not None else None
+        self.args = []
+        for l, L in enumerate(step.layers):
+            a = _abi.cb_attn_args()
+            a.out, a.q = L.out.data_ptr(), L.q.data_ptr()
+            a.k_cache, a.v_cache = L.k_cache.data_ptr(), L.v_cache.data_ptr()
+            a.shape = self.shapes[l]
+            a.num_pages = L.k_cache.shape[0]
+            a.scale = float(step.scale)
+            a.workspace = L.workspace.data_ptr() if L.workspace is not None else None
+            a.workspace_bytes = L.workspace.numel() if L.workspace is not None else 0
+            self.args.append(a)
+        self.append_args = [(L.k_cache.data_ptr(), L.v_cache.data_ptr(), L.k_new.data_ptr(), L.v_new.data_ptr(),
+                             L.k_cache.shape[0], L.k_new.shape[0]) for L in step.layers]
+        self.dtype = dt
 
     def prepare(self):
         """Host half of a step: schedule + plan into the next pinned buffer and enqueue its copy to the device on
@@ -244,7 +272,7 @@ class StepPipeline:
         i = self.k % 2
         self.k += 1
         if self.copied[i] is not None:
-            self.copied[i].synchronize()
+            self.copied[i].synchronize()   # the pinned half of pair i is free again
         host = self.host[i].numpy()
         hs = self.sched.build_into(host[:self.meta_cap])
         N, T = hs.num_reqs, hs.num_tokens
@@ -258,37 +286,58 @@ class StepPipeline:
             plans.append((p, at))
             at += int(p.info.used)
         dev = self.dev[i]
-        dev[:at].copy_(self.host[i][:at], non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record(self.main)
+        ev = self.copy_ev[i]
+        if self.copier is not None:
+            # the copy waits only for the step that last read this device buffer, then runs beside the kernels of
+            # the step in flight; the compute stream waits for it before this step's first kernel
+            if self.released[i] is not None:
+                self.copier.wait_event(self.released[i])
+            with torch.cuda.stream(self.copier):
+                dev[:at].copy_(self.host[i][:at], non_blocking=True)
+            ev.record(self.copier)
+            self.main.wait_event(ev)
+        else:
+            dev[:at].copy_(self.host[i][:at], non_blocking=True)
+            ev.record(self.main)
         self.copied[i] = ev
+        self.cur = i
+        base = dev.data_ptr()
         views = []
         for l in range(len(self.w.layers)):
-            w_ = hs.table_width[l]
-            bt = dev[hs.off_block_table[l]:hs.off_block_table[l] + N * w_].view(N, w_)
-            sm = dev[hs.off_slot_mapping[l]:hs.off_slot_mapping[l] + T]
             p, off = plans[l]
-            views.append((bt, sm, p, dev[off:off + int(p.info.used)]))
+            views.append((base + 4 * int(hs.off_block_table[l]), int(hs.table_width[l]),
+                          base + 4 * int(hs.off_slot_mapping[l]), p.info, base + 4 * off))
+        self.num_tokens = T
         return views
+
+    def _check(self, status, what):
+        if status != 0:
+            raise CbError(status, what)
 
     def run(self, events=None):
         """One full step. `events`, if given, holds per layer 6 timing events: decode start/end (compute stream),
         prefill start/end (the stream running the prefill-tile and per-token kernels), merge start/end."""
-        st = self.step
+        lib = self.lib
         views = self.prepare()
         main = self.main
-        for l, (bt, sm, plan, pdev) in enumerate(views):
-            L = st.layers[l]
-            kv_append(L.k_cache, L.v_cache, L.k_new, L.v_new, sm)
+        w = self.w
+        T = self.num_tokens
+        for l, (bt, width, sm, info, plan) in enumerate(views):
+            kc, vc, kn, vn, n_pages, rows = self.append_args[l]
+            if T > rows:
+                raise ValueError("step has more new tokens than the pipeline's input rows")
+            self._check(lib.cb_kv_append(kc, vc, kn, vn, sm, T, n_pages, w.page_size, w.Hkv, w.D, self.dtype,
+                                         self.h_main), "cb_kv_append")
 
-        def attend(l, phases, ev0=None, ev1=None, stream=None):
-            bt, sm, plan, pdev = views[l]
-            L = st.layers[l]
-            s = stream or main
+        def attend(l, phases, ev0=None, ev1=None, aux=False):
+            bt, width, sm, info, plan = views[l]
+            a = self.args[l]
+            a.block_table, a.table_width, a.plan, a.plan_info, a.phases = bt, width, plan, info, phases
+            s = self.aux if aux else main
             if ev0 is not None:
                 ev0.record(s)
-            paged_attention(L.out, L.q, L.k_cache, L.v_cache, bt, plan, pdev, st.scale, L.workspace, stream=s,
-                            phases=phases)
+            self._check(lib.cb_paged_attention(C.byref(a), self.h_aux if aux else self.h_main),
+                        "cb_paged_attention")
             if ev1 is not None:
                 ev1.record(s)
 
@@ -299,7 +348,7 @@ class StepPipeline:
             self.fork.record(main)
             self.aux.wait_event(self.fork)
             for l in range(n):
-                attend(l, pre, E(l, 2), E(l, 3), self.aux)
+                attend(l, pre, E(l, 2), E(l, 3), aux=True)
             for l in range(n):
                 attend(l, CB_PHASE_DECODE, E(l, 0), E(l, 1))
             self.join.record(self.aux)
@@ -310,3 +359,7 @@ class StepPipeline:
                 attend(l, pre, E(l, 2), E(l, 3))
         for l in range(n):
             attend(l, CB_PHASE_COMBINE, E(l, 4), E(l, 5))
+        if self.copier is not None:
+            rel = self.rel_ev[self.cur]
+            rel.record(main)
+            self.released[self.cur] = rel

@@ -175,3 +175,23 @@ def test_deterministic_and_batch_invariant(torch_gpu):
     alone.requests[0].pages = [w.requests[0].pages[0]]
     c = _run(alone, decode_split=256, prefill_split=512)
     assert torch_gpu.equal(a.layers[0].out[0], c.layers[0].out[0])
+
+
+@pytest.mark.parametrize("mode", ["copy stream", "copy on compute stream", "concurrent prefill"])
+def test_pipeline_steps_match_oracle(torch_gpu, mode):
+    """The benchmark's loop: steps prepared into alternating pinned/device buffers, launched with the lean path,
+    repeated; every repetition of the (unchanged) step must produce the oracle's rows."""
+    from paged_kv_attention_varlen_amd.step import Step, StepPipeline
+    for idx in (3, 5):
+        w = make_workload(idx, mini=True)
+        st = Step.from_workload(w)
+        pipe = StepPipeline(w, st, copy_stream=(mode != "copy on compute stream"),
+                            concurrent=(mode == "concurrent prefill"))
+        for l in range(len(w.layers)):
+            st.layers[l].out.fill_(float("nan"))
+        for _ in range(3):
+            pipe.run()
+        torch_gpu.cuda.synchronize()
+        print(f"[gpu] pipeline {mode} workload {idx}", flush=True)
+        for l in range(len(w.layers)):
+            H.compare(w, st, l, label=f"pipeline {mode} w{idx} layer {l}")
