@@ -520,6 +520,7 @@ constexpr int kPfRows = 128;   // query rows of one work group: 4 waves x 32
 constexpr int kPfKeys = 64;    // keys per tile
 constexpr int kPrefillMaxPages = 1536;   // page ids of one prefill item staged in LDS (split / page + 2)
 constexpr float kRescaleSlack = 8.f;     // log2 units the running maximum may lag behind the true one
+constexpr float kWeightSumBound = 256.f; // 2^kRescaleSlack: a half's weight sum above it sends the row to the rare path
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -718,13 +719,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
             return sum;
         };
-        // Softmax of one half against the current running maximum (speculative): the row maximum, the bf16 weights
-        // (the B operands of the PV product) and their sum. Returns whether the running maximum must move.
-        auto softmax_half = [&](const f32x16 &S, bf16x8 (&pf)[2], float &lsum, float &tmax) {
-            float x = fmaxf(S[0], S[1]);
-#pragma unroll
-            for (int v = 2; v < 16; ++v) x = fmaxf(x, S[v]);
-            tmax = max_xor32(x) * scale_log2e;
+        // Softmax of one half against the current running maximum (speculative): the bf16 weights (the B operands
+        // of the PV product) and their sum. The weights are trusted when the row already has a maximum and their sum
+        // stays below 2^kRescaleSlack, which bounds every weight; otherwise (first visible keys of the row, or scores
+        // that climbed past the running maximum) the rare path below settles the row. No row maximum is computed on
+        // the common path.
+        auto softmax_half = [&](const f32x16 &S, bf16x8 (&pf)[2], float &lsum) {
             lsum = weights(S, m == kNegInf ? 0.f : m, pf);
             // pin the speculative results here, beside the matrix work of this region: otherwise the compiler sinks
             // them past the rare-path branch that follows and they no longer overlap the MFMAs
@@ -735,17 +735,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 pf[kk] = as_bf16x8(t);
             }
             asm volatile("" : "+v"(lsum));
-            return tmax > m + kRescaleSlack;
+            // !(lsum <= bound) also catches a sum that overflowed to inf or NaN
+            return (m == kNegInf && lsum > 0.f) || !(lsum <= kWeightSumBound);
         };
-        // Rare path: some row's maximum moved by more than the slack. Move it, rescale the row's accumulators and
-        // recompute its weights.
-        auto settle = [&](bool bump, const f32x16 &S, bf16x8 (&pf)[2], float &lsum, float tmax) {
+        // Rare path for the rows that asked for it: take the half's true row maximum (both lanes of the row), move
+        // the running maximum up to it if it is higher, rescale the row's accumulators and recompute its weights.
+        auto settle = [&](bool want, f32x16 &S, bf16x8 (&pf)[2], float &lsum) {
             // a loop of at most one trip rather than a branch, so that the compiler keeps the rescale out of line
-            const int trips = __builtin_amdgcn_ballot_w64(bump) ? 1 : 0;
+            const int trips = __builtin_amdgcn_ballot_w64(want) ? 1 : 0;
 #pragma nounroll
             for (int t = 0; t < trips; ++t) {
-                const float m_new = bump ? tmax : m;
-                const float alpha = bump ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+                float x = S[0];
+#pragma unroll
+                for (int v = 1; v < 16; ++v) x = __builtin_elementwise_maximum(x, S[v]);
+                // the partner lane of the row decides too: both see the same maximum
+                const float tmax = max_xor32(x) * scale_log2e;
+                const bool bump = __shfl_xor(int(want), 32) != 0 || want;
+                const float m_new = bump ? fmaxf(m, tmax) : m;
+                const float alpha = m_new > m ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
                 l *= alpha;
 #pragma unroll
                 for (int b = 0; b < DB; ++b) acc[b] *= alpha;
@@ -766,16 +773,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
             f32x16 S0, S1;
             bf16x8 p0[2], p1[2];
-            float ls0, ls1, tm0, tm1;
+            float ls0, ls1;
             qk_half(kcur, 0, S0);
             if (edge) mask_half(S0, tile * kPfKeys);
             qk_half(kcur, 1, S1);
-            const bool b0 = softmax_half(S0, p0, ls0, tm0);
-            settle(b0, S0, p0, ls0, tm0);
+            const bool b0 = softmax_half(S0, p0, ls0);
+            settle(b0, S0, p0, ls0);
             if (edge) mask_half(S1, tile * kPfKeys + 32);
             pv_half(vcur, 0, p0);
-            const bool b1 = softmax_half(S1, p1, ls1, tm1);
-            settle(b1, S1, p1, ls1, tm1);
+            const bool b1 = softmax_half(S1, p1, ls1);
+            settle(b1, S1, p1, ls1);
             pv_half(vcur, 1, p1);
             // the next tile has landed for every wave; every wave is done with this one
             wait_vmem();
