@@ -774,6 +774,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             f32x16 S0, S1;
             bf16x8 p0[2], p1[2];
             float ls0, ls1;
+            // the compute of a tile runs at raised wave priority: while this work group's waves compute, the other
+            // work group on the CU, if it is copying, waiting or at its barrier, does not take issue slots first
+            __builtin_amdgcn_s_setprio(1);
             qk_half(kcur, 0, S0);
             if (edge) mask_half(S0, tile * kPfKeys);
             qk_half(kcur, 1, S1);
@@ -784,6 +787,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const bool b1 = softmax_half(S1, p1, ls1);
             settle(b1, S1, p1, ls1);
             pv_half(vcur, 1, p1);
+            __builtin_amdgcn_s_setprio(0);
             // the next tile has landed for every wave; every wave is done with this one
             wait_vmem();
             __syncthreads();
