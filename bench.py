@@ -7,8 +7,8 @@ A step is the whole hot path over one synthetic batch: host scheduling and plann
 host-to-device metadata copy, the KV append, split-KV decode, prefill tiles and the merge of split rows, for every
 layer of the workload. Kernels run back to back on one compute stream; the host prepares step k+1 (into the other
 of two pinned/device buffer pairs, copied on a stream of its own) while the device runs step k. Per-kernel durations
-come from HIP events recorded on the compute stream around the decode and prefill kernels of every step and around
-the merge on every COMBINE_EVERY-th step. --concurrent instead runs the prefill-tile kernels on a second stream
+come from HIP events recorded on the compute stream around the decode, prefill and merge kernels of every
+EVENTS_EVERY-th timed step. --concurrent instead runs the prefill-tile kernels on a second stream
 beside the decode kernel (their event intervals then overlap). Inputs (caches with the history, the step's new
 Q/K/V rows) are resident in HBM before timing starts.
 
@@ -34,7 +34,7 @@ METRIC = "mixed-batch paged attention: query tokens/s + KV GB/s (% HBM / % MFMA 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-COMBINE_EVERY = 8              # steps between timed merge launches
+EVENTS_EVERY = 4               # every EVENTS_EVERY-th timed step carries the per-kernel timing events
 WARMUP_SECONDS = 0.3           # minimum duration of the untimed warm-up
 DEVICE_SRC = os.path.join(ROOT, "paged_kv_attention_varlen_amd", "csrc", "cb_device.hip")
 
@@ -199,32 +199,29 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] {warm} warm-up steps")
     L = len(w.layers)
-    # Every step brackets the decode and prefill kernels with events (4 per layer); the merge is bracketed on every
-    # COMBINE_EVERY-th step only: each event is a packet in the stream and costs the step a little time.
-    def step_events(k):
-        n = 6 if k % COMBINE_EVERY == 0 else 4
-        return [[torch.cuda.Event(enable_timing=True) for _ in range(n)] + [None] * (6 - n) for _ in range(L)]
-    events = [step_events(k) for k in range(args.steps)]
+    # Every EVENTS_EVERY-th timed step brackets its decode, prefill and merge kernels with events (6 per layer); the
+    # kernel averages come from that sample of the timed steps. Each event is a packet in the stream and costs the
+    # step a few microseconds, so the other steps run without them.
+    timed = list(range(0, args.steps, EVENTS_EVERY))
+    events = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)] for k in timed}
     # torch creates the HIP event on its first record: do that here, outside the timed region
-    for per_step in events:
+    for per_step in events.values():
         for per_layer in per_step:
             for ev in per_layer:
-                if ev is not None:
-                    ev.record()
+                ev.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        pipe.run(events[k])
+        pipe.run(events.get(k))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step")
 
     # per-kernel durations from the events (same stream as the launches)
-    dec_ms = [[events[k][l][0].elapsed_time(events[k][l][1]) for k in range(args.steps)] for l in range(L)]
-    pre_ms = [[events[k][l][2].elapsed_time(events[k][l][3]) for k in range(args.steps)] for l in range(L)]
-    com_ms = [[events[k][l][4].elapsed_time(events[k][l][5]) for k in range(0, args.steps, COMBINE_EVERY)]
-              for l in range(L)]
+    dec_ms = [[events[k][l][0].elapsed_time(events[k][l][1]) for k in timed] for l in range(L)]
+    pre_ms = [[events[k][l][2].elapsed_time(events[k][l][3]) for k in timed] for l in range(L)]
+    com_ms = [[events[k][l][4].elapsed_time(events[k][l][5]) for k in timed] for l in range(L)]
     work = algorithmic_work(w, sched)
     T = sched["num_tokens"]
     value = T / (ms_per_step / 1e3)
@@ -239,7 +236,8 @@ def main():
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": stored_traffic(), "algorithmic_bytes_per_step": dec_b,
                     "launches_per_step": sum(1 for x in work if x["decodes"]),
-                    "avg_launch_us": round(dec_t * 1e3 / max(1, sum(1 for x in work if x["decodes"])), 2)}
+                    "avg_launch_us": round(dec_t * 1e3 / max(1, sum(1 for x in work if x["decodes"])), 2),
+                    "timed_steps_sampled": len(timed)}
     pre_t = sum(float(np.mean(pre_ms[l])) for l in range(L))
     pre_f = sum(x["prefill_flops"] for x in work)
     roofline_prefill = None
@@ -247,7 +245,8 @@ def main():
         tf = pre_f / (pre_t / 1e3) / 1e12
         roofline_prefill = {"bound": "mfma", "kernel": "prefill_kernel (bf16 MFMA tiles)", "achieved": round(tf, 1),
                             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                            "algorithmic_flops_per_step": pre_f, "avg_launch_us": round(pre_t * 1e3 / L, 2)}
+                            "algorithmic_flops_per_step": pre_f, "avg_launch_us": round(pre_t * 1e3 / L, 2),
+                            "timed_steps_sampled": len(timed)}
 
     base = None
     if not args.no_cpu_baseline:
