@@ -144,6 +144,9 @@ def main():
     ap.add_argument("--no-copy-stream", action="store_true",
                     help="copy each step's metadata on the compute stream instead of a stream of its own (which lets "
                          "the copy overlap the previous step's kernels)")
+    ap.add_argument("--graphs", action="store_true",
+                    help="replay each step's kernels as a captured HIP graph (steps that carry timing events run "
+                         "eagerly)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, run a plain device copy of this many MiB three times (untimed), the "
                          "known-size reference for scaling HBM byte counters")
@@ -184,7 +187,7 @@ def main():
     t = time.time()
     step = Step.from_workload(w, decode_split=args.decode_split, prefill_split=args.prefill_split, threads=16)
     pipe = StepPipeline(w, step, args.decode_split, args.prefill_split, concurrent=args.concurrent,
-                        copy_stream=not args.no_copy_stream)
+                        copy_stream=not args.no_copy_stream, graphs=args.graphs)
     sched = step.sched
     log(f"[bench] setup {time.time() - t:.1f}s; N={sched['num_reqs']} T={sched['num_tokens']} "
         f"decodes={sched['num_decodes']}; plans {[L.plan.counts() for L in step.layers]}")

@@ -203,11 +203,12 @@ class StepPipeline:
     concurrent=True runs the prefill-tile and per-token kernels on a second compute stream beside the decode kernel
     (decode streams HBM while prefill keeps the matrix cores busy) and joins both before the merge. copy_stream=True
     moves the metadata copy to a stream of its own, so that it overlaps the previous step's kernels instead of
-    sitting between steps. All streams have the default priority.
+    sitting between steps. graphs=True replays the step's kernels as a captured HIP graph whenever the step's launch
+    configuration (metadata buffer, plans, token count) was seen before. All streams have the default priority.
     """
 
     def __init__(self, w, step: Step, decode_split: int = 0, prefill_split: int = 0, concurrent: bool = False,
-                 copy_stream: bool = True):
+                 copy_stream: bool = True, graphs: bool = False):
         from . import Scheduler
         torch = _torch()
         self.step = step
@@ -262,6 +263,8 @@ class StepPipeline:
         self.append_args = [(L.k_cache.data_ptr(), L.v_cache.data_ptr(), L.k_new.data_ptr(), L.v_new.data_ptr(),
                              L.k_cache.shape[0], L.k_new.shape[0]) for L in step.layers]
         self.dtype = dt
+        self.use_graphs = graphs
+        self.graphs = {}
 
     def prepare(self):
         """Host half of a step: schedule + plan into the next pinned buffer and enqueue its copy to the device on
@@ -314,12 +317,9 @@ class StepPipeline:
         if status != 0:
             raise CbError(status, what)
 
-    def run(self, events=None):
-        """One full step. `events`, if given, holds per layer 6 timing events: decode start/end (compute stream),
-        prefill start/end (the stream running the prefill-tile and per-token kernels), merge start/end."""
+    def _launch(self, views, stream, handle, events=None):
+        """Enqueue the step's kernels for the prepared metadata `views` on `stream` (C handle `handle`)."""
         lib = self.lib
-        views = self.prepare()
-        main = self.main
         w = self.w
         T = self.num_tokens
         for l, (bt, width, sm, info, plan) in enumerate(views):
@@ -327,17 +327,16 @@ class StepPipeline:
             if T > rows:
                 raise ValueError("step has more new tokens than the pipeline's input rows")
             self._check(lib.cb_kv_append(kc, vc, kn, vn, sm, T, n_pages, w.page_size, w.Hkv, w.D, self.dtype,
-                                         self.h_main), "cb_kv_append")
+                                         handle), "cb_kv_append")
 
         def attend(l, phases, ev0=None, ev1=None, aux=False):
             bt, width, sm, info, plan = views[l]
             a = self.args[l]
             a.block_table, a.table_width, a.plan, a.plan_info, a.phases = bt, width, plan, info, phases
-            s = self.aux if aux else main
+            s = self.aux if aux else stream
             if ev0 is not None:
                 ev0.record(s)
-            self._check(lib.cb_paged_attention(C.byref(a), self.h_aux if aux else self.h_main),
-                        "cb_paged_attention")
+            self._check(lib.cb_paged_attention(C.byref(a), self.h_aux if aux else handle), "cb_paged_attention")
             if ev1 is not None:
                 ev1.record(s)
 
@@ -345,20 +344,51 @@ class StepPipeline:
         E = (lambda l, k: events[l][k]) if events else (lambda l, k: None)
         pre = CB_PHASE_ROWWISE | CB_PHASE_PREFILL
         if self.concurrent:
-            self.fork.record(main)
+            self.fork.record(stream)
             self.aux.wait_event(self.fork)
             for l in range(n):
                 attend(l, pre, E(l, 2), E(l, 3), aux=True)
             for l in range(n):
                 attend(l, CB_PHASE_DECODE, E(l, 0), E(l, 1))
             self.join.record(self.aux)
-            main.wait_event(self.join)
+            stream.wait_event(self.join)
         else:
             for l in range(n):
                 attend(l, CB_PHASE_DECODE, E(l, 0), E(l, 1))
                 attend(l, pre, E(l, 2), E(l, 3))
         for l in range(n):
             attend(l, CB_PHASE_COMBINE, E(l, 4), E(l, 5))
+
+    def _graph_for(self, views):
+        """The step's kernels captured as a HIP graph, cached by everything their launches depend on: the metadata
+        buffer (its device address), the plans (item counts, split sizes, section offsets), the block-table width
+        and the token count. A step whose launch configuration was seen before replays its graph."""
+        torch = _torch()
+        key = (self.cur, self.num_tokens) + tuple(
+            (bt, width, sm, plan, bytes(info)) for (bt, width, sm, info, plan) in views)
+        g = self.graphs.get(key)
+        if g is None:
+            side = torch.cuda.Stream(self.main.device)
+            side.wait_stream(self.main)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side):
+                g.capture_begin()
+                self._launch(views, side, C.c_void_p(side.cuda_stream))
+                g.capture_end()
+            self.main.wait_stream(side)
+            self.graphs[key] = g
+        return g
+
+    def run(self, events=None):
+        """One full step. `events`, if given, holds per layer 6 timing events: decode start/end (compute stream),
+        prefill start/end (the stream running the prefill-tile and per-token kernels), merge start/end. With
+        graphs=True the step replays a captured graph, except when it carries events (then it runs eagerly)."""
+        views = self.prepare()
+        main = self.main
+        if self.use_graphs and events is None and not self.concurrent:
+            self._graph_for(views).replay()
+        else:
+            self._launch(views, main, self.h_main, events)
         if self.copier is not None:
             rel = self.rel_ev[self.cur]
             rel.record(main)

@@ -177,7 +177,7 @@ def test_deterministic_and_batch_invariant(torch_gpu):
     assert torch_gpu.equal(a.layers[0].out[0], c.layers[0].out[0])
 
 
-@pytest.mark.parametrize("mode", ["copy stream", "copy on compute stream", "concurrent prefill"])
+@pytest.mark.parametrize("mode", ["copy stream", "copy on compute stream", "concurrent prefill", "graph replay"])
 def test_pipeline_steps_match_oracle(torch_gpu, mode):
     """The benchmark's loop: steps prepared into alternating pinned/device buffers, launched with the lean path,
     repeated; every repetition of the (unchanged) step must produce the oracle's rows."""
@@ -186,12 +186,16 @@ def test_pipeline_steps_match_oracle(torch_gpu, mode):
         w = make_workload(idx, mini=True)
         st = Step.from_workload(w)
         pipe = StepPipeline(w, st, copy_stream=(mode != "copy on compute stream"),
-                            concurrent=(mode == "concurrent prefill"))
-        for l in range(len(w.layers)):
-            st.layers[l].out.fill_(float("nan"))
-        for _ in range(3):
-            pipe.run()
-        torch_gpu.cuda.synchronize()
+                            concurrent=(mode == "concurrent prefill"), graphs=(mode == "graph replay"))
         print(f"[gpu] pipeline {mode} workload {idx}", flush=True)
-        for l in range(len(w.layers)):
-            H.compare(w, st, l, label=f"pipeline {mode} w{idx} layer {l}")
+        # every repetition is checked; graph replays (from the third step on) alternate with eager work on the
+        # same stream and host synchronisations
+        for rep in range(5):
+            for l in range(len(w.layers)):
+                st.layers[l].out.fill_(float("nan"))
+            pipe.run()
+            torch_gpu.cuda.synchronize()
+            for l in range(len(w.layers)):
+                H.compare(w, st, l, label=f"pipeline {mode} w{idx} layer {l} repetition {rep}")
+        if mode == "graph replay":
+            assert len(pipe.graphs) == 2, "one graph per metadata buffer"
