@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 1
+#define CB_ABI_VERSION 2
 
 typedef int32_t cb_status;
 #define CB_OK 0
@@ -87,17 +87,24 @@ typedef struct cb_layer_pool {
     const int32_t *free_pages; /* host array: free pages in allocation order; pages are taken from the front   */
 } cb_layer_pool;
 
+/* Scheduling policies (Transformers "continuous batching architecture" page, sections "FIFO" and "PrefillFirst"). */
+#define CB_POLICY_FIFO 0           /* active decodes, then active prefills, then waiting requests                 */
+#define CB_POLICY_PREFILL_FIRST 1  /* active prefills, then waiting requests, then decodes with what budget is left */
+
 typedef struct cb_sched_params {
     int32_t max_batch_tokens;  /* token budget of one forward pass, >= 1                                        */
     int32_t max_requests;      /* request cap of one forward pass, >= 1                                         */
     int32_t page_size;         /* tokens per page, >= 1                                                         */
     int32_t pad_page;          /* page id written into unused block-table entries (a reserved padding page)     */
     int32_t n_layers;          /* 1 or 2 layer types                                                            */
-    float safety_margin;       /* hold new prefills while any pool's free fraction is below this (0 disables)  */
+    int32_t policy;            /* CB_POLICY_FIFO or CB_POLICY_PREFILL_FIRST                                     */
+    float safety_margin;       /* hold new prefills while any pool's free fraction is below this (0 disables);
+                                  the page gives 0.15 as the FIFO default and 0 for PrefillFirst              */
 } cb_sched_params;
 
 /* Header of the packed int32 buffer cb_build_metadata writes. Offsets count int32 elements from the buffer start;
- * per scheduled row r (schedule order: decodes, then continuing prefills, then admitted requests): */
+ * per scheduled row r (rows laid out decodes first, then continuing prefills, then admitted requests, each group in
+ * scheduling order, whatever the policy): */
 typedef struct cb_step {
     int32_t num_reqs;                        /* N rows scheduled                                                 */
     int32_t num_tokens;                      /* T                                                                */
@@ -111,7 +118,7 @@ typedef struct cb_step {
     int64_t off_query_start_loc;             /* [N+1]                                                            */
     int64_t off_seq_lens;                    /* [N]                                                              */
     int64_t off_req_index;                   /* [N] input index of each row                                      */
-    int64_t off_stalled;                     /* [n_stalled] input indices                                        */
+    int64_t off_stalled;                     /* [n_stalled] input indices, ascending                             */
     int64_t off_block_table[CB_MAX_LAYERS];  /* [N][table_width]; unused entries hold pad_page                   */
     int64_t off_slot_mapping[CB_MAX_LAYERS]; /* [T] page * page_size + offset of each new token's K/V            */
     int64_t off_ring_len[CB_MAX_LAYERS];     /* [N] ring length per row (0 for full layers)                      */
@@ -119,15 +126,16 @@ typedef struct cb_step {
 } cb_step;
 
 /*
- * Schedule one step (Transformers "continuous batching architecture" page, sections "调度器", "FIFO", "准入" and
- * "分块预填充"; "Continuous Batching" blog, section "扩展：与 Chunked Prefill 结合"):
- *   1. active decodes in FIFO order, one token each;
- *   2. active prefills, each continuing with min(num_pending, budget left) tokens;
- *   3. waiting requests in arrival order: held while a pool's free fraction is below safety_margin; admitted
+ * Schedule one step (Transformers "continuous batching architecture" page, sections "调度器", "FIFO",
+ * "PrefillFirst", "准入" and "分块预填充"; "Continuous Batching" blog, section "扩展：与 Chunked Prefill 结合").
+ * Three passes, in the order of the policy (FIFO: D, P, A; PrefillFirst: P, A, D):
+ *   D. active decodes in arrival order, one token each;
+ *   P. active prefills, each continuing with min(num_pending, budget left) tokens;
+ *   A. waiting requests in arrival order: held while a pool's free fraction is below safety_margin; admitted
  *      all-or-nothing across layer types (pages for the chunk, plus a whole ring for sliding layers); the first
  *      refusal stops admission.
- *   Every pass stops at max_requests rows or an exhausted budget. Active requests whose pages cannot be allocated
- *   are reported stalled and left out.
+ *   Every pass stops at max_requests rows or an exhausted budget, and takes its pages from the front of the free
+ *   lists in that order. Active requests whose pages cannot be allocated are reported stalled and left out.
  * Pure host function: reads reqs/params/layers, writes `out` (capacity out_capacity int32 elements) and `step`.
  * Returns CB_OK, CB_E_INVAL (inconsistent input, including a ring too small for max_batch_tokens), CB_E_NOSPACE
  * (no row could be scheduled because pages ran out; out/step are still valid) or CB_E_CAPACITY (step->used tells

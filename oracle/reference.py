@@ -22,7 +22,7 @@ def schedule(w):
                "pool_pages": l.num_pages - len(l.padding_pages), "free_pages": l.free_pages} for l in w.layers]
     pad = w.layers[0].padding_pages[0] if w.layers[0].padding_pages else 0
     return S.build_metadata(w.requests, layers, w.max_batch_tokens, w.max_requests, w.page_size,
-                            w.safety_margin, pad)
+                            w.safety_margin, pad, policy=w.policy)
 
 
 def history_range(w, layer: int, ctx: int):

@@ -38,13 +38,24 @@ def ring_is_large_enough(ring_len, window_left, max_chunk, page_size):
     return ring_len >= (window_left + max_chunk + page_size - 2) // page_size + 1
 
 
-def build_metadata(requests, layers, max_batch_tokens, max_requests, page_size, safety_margin=0.0, pad_page=0):
+FIFO, PREFILL_FIRST = "fifo", "prefill_first"
+
+
+def build_metadata(requests, layers, max_batch_tokens, max_requests, page_size, safety_margin=0.0, pad_page=0,
+                   policy=FIFO):
     """Schedule one step.
 
     requests: sequence with .state, .num_computed, .num_pending, .pages (list per layer), in arrival order.
     layers: sequence of dicts {ring_len, window_left, pool_pages, free_pages}.
+    policy: FIFO fills the budget with active decodes, then active prefills, then waiting requests (Transformers
+    "continuous batching architecture" page, section "FIFO"); PREFILL_FIRST finishes prefill work before decodes
+    resume (section "PrefillFirst"). Reading taken: active prefills, then waiting requests, then decodes with what
+    is left of the budget; pages are taken from the free lists in that order. Either way the rows are laid out
+    decodes first, then continuing prefills, then admitted requests, each group in scheduling order.
     Returns a dict (see module docstring); "status" is "ok", "inval" or "nospace".
     """
+    if policy not in (FIFO, PREFILL_FIRST):
+        return {"status": E_INVAL}
     P = page_size
     L = len(layers)
     if P < 1 or max_batch_tokens < 1 or max_requests < 1 or L < 1:
@@ -90,57 +101,71 @@ def build_metadata(requests, layers, max_batch_tokens, max_requests, page_size, 
             taken[l] += nd[l]
         return got
 
-    rows = []          # (request index, q_len, new pages per layer)
+    rows = {DECODING: [], PREFILLING: [], WAITING: []}   # (request index, q_len, new pages per layer)
     stalled = []
     first_rejected = -1
     held = False
     budget = max_batch_tokens
 
-    # 1) active decodes, one token each
-    for i, rq in enumerate(requests):
-        if rq.state != DECODING:
-            continue
-        if len(rows) >= max_requests or budget < 1:
-            break
-        nd = needs(rq, 1)
-        if not fits(nd):
-            stalled.append(i)
-            continue
-        rows.append((i, 1, take(nd)))
-        budget -= 1
-    num_decodes = len(rows)
+    def n_rows():
+        return sum(len(v) for v in rows.values())
 
-    # 2) active prefills, continuing where they stopped
-    for i, rq in enumerate(requests):
-        if rq.state != PREFILLING:
-            continue
-        if len(rows) >= max_requests or budget < 1:
-            break
-        q = min(rq.num_pending, budget)
-        nd = needs(rq, q)
-        if not fits(nd):
-            stalled.append(i)
-            continue
-        rows.append((i, q, take(nd)))
-        budget -= q
+    def decodes():
+        """active decodes, one token each"""
+        nonlocal budget
+        for i, rq in enumerate(requests):
+            if rq.state != DECODING:
+                continue
+            if n_rows() >= max_requests or budget < 1:
+                break
+            nd = needs(rq, 1)
+            if not fits(nd):
+                stalled.append(i)
+                continue
+            rows[DECODING].append((i, 1, take(nd)))
+            budget -= 1
 
-    # 3) waiting requests in arrival order (admission)
-    for i, rq in enumerate(requests):
-        if rq.state != WAITING:
-            continue
-        if len(rows) >= max_requests or budget < 1:
-            break
-        if any(lay["pool_pages"] > 0 and (len(free[l]) - taken[l]) < safety_margin * lay["pool_pages"]
-               for l, lay in enumerate(layers)):
-            held = True
-            break
-        q = min(rq.num_pending, budget)
-        nd = needs(rq, q)
-        if not fits(nd):
-            first_rejected = i
-            break
-        rows.append((i, q, take(nd)))
-        budget -= q
+    def prefills():
+        """active prefills, continuing where they stopped"""
+        nonlocal budget
+        for i, rq in enumerate(requests):
+            if rq.state != PREFILLING:
+                continue
+            if n_rows() >= max_requests or budget < 1:
+                break
+            q = min(rq.num_pending, budget)
+            nd = needs(rq, q)
+            if not fits(nd):
+                stalled.append(i)
+                continue
+            rows[PREFILLING].append((i, q, take(nd)))
+            budget -= q
+
+    def admit():
+        """waiting requests in arrival order (admission)"""
+        nonlocal budget, held, first_rejected
+        for i, rq in enumerate(requests):
+            if rq.state != WAITING:
+                continue
+            if n_rows() >= max_requests or budget < 1:
+                break
+            if any(lay["pool_pages"] > 0 and (len(free[l]) - taken[l]) < safety_margin * lay["pool_pages"]
+                   for l, lay in enumerate(layers)):
+                held = True
+                break
+            q = min(rq.num_pending, budget)
+            nd = needs(rq, q)
+            if not fits(nd):
+                first_rejected = i
+                break
+            rows[WAITING].append((i, q, take(nd)))
+            budget -= q
+
+    for stage in ((decodes, prefills, admit) if policy == FIFO else (prefills, admit, decodes)):
+        stage()
+    stalled.sort()
+    num_decodes = len(rows[DECODING])
+    rows = rows[DECODING] + rows[PREFILLING] + rows[WAITING]
 
     N = len(rows)
     q_lens = np.array([q for _, q, _ in rows], dtype=np.int64)

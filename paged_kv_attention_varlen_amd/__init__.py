@@ -18,8 +18,10 @@ import numpy as np
 
 from . import _abi
 from ._abi import (CB_DECODING, CB_DTYPE_BF16, CB_DTYPE_F32, CB_E_CAPACITY, CB_E_NOSPACE, CB_OK,  # noqa: F401
-                   CB_PHASE_COMBINE, CB_PHASE_DECODE, CB_PHASE_PREFILL, CB_PHASE_ROWWISE, CB_PREFILLING, CB_WAITING,
-                   CbError)
+                   CB_PHASE_COMBINE, CB_PHASE_DECODE, CB_PHASE_PREFILL, CB_PHASE_ROWWISE, CB_POLICY_FIFO,
+                   CB_POLICY_PREFILL_FIRST, CB_PREFILLING, CB_WAITING, CbError)
+
+POLICIES = {"fifo": CB_POLICY_FIFO, "prefill_first": CB_POLICY_PREFILL_FIRST}
 
 __all__ = ["build_metadata", "plan_attention", "kv_append", "paged_attention", "workspace_size", "AttnPlan",
            "Scheduler", "plan_into", "load_library", "CbError"]
@@ -40,8 +42,8 @@ def _ptr(a: np.ndarray):
 # ------------------------------------------------------------------------------------------- cb_build_metadata
 
 def build_metadata(requests, layers, max_batch_tokens: int, max_requests: int, page_size: int,
-                   safety_margin: float = 0.0, pad_page: int = 0) -> dict:
-    """Schedule one step (cb_build_metadata).
+                   safety_margin: float = 0.0, pad_page: int = 0, policy: str = "fifo") -> dict:
+    """Schedule one step (cb_build_metadata). policy: "fifo" or "prefill_first".
 
     requests: sequence of objects with .id, .state (0 decoding / 1 prefilling / 2 waiting), .num_computed,
       .num_pending and .pages (one int array per layer), in arrival order.
@@ -73,7 +75,7 @@ def build_metadata(requests, layers, max_batch_tokens: int, max_requests: int, p
         pools[l].n_free = f.size
         pools[l].free_pages = _ptr(f)
     params = _abi.cb_sched_params(int(max_batch_tokens), int(max_requests), int(page_size), int(pad_page), L,
-                                  float(safety_margin))
+                                  POLICIES[policy], float(safety_margin))
     step = _abi.cb_step()
     cap = 4096
     while True:
@@ -107,7 +109,7 @@ class Scheduler:
     host memory that is then copied to the device in one transfer)."""
 
     def __init__(self, requests, layers, max_batch_tokens: int, max_requests: int, page_size: int,
-                 safety_margin: float = 0.0, pad_page: int = 0):
+                 safety_margin: float = 0.0, pad_page: int = 0, policy: str = "fifo"):
         self._lib = _abi.load()
         self._keep = []
         n, L = len(requests), len(layers)
@@ -129,7 +131,7 @@ class Scheduler:
             self.pools[l] = _abi.cb_layer_pool(int(lay["ring_len"]), int(lay["window_left"]), int(lay["pool_pages"]),
                                                f.size, _ptr(f))
         self.params = _abi.cb_sched_params(int(max_batch_tokens), int(max_requests), int(page_size), int(pad_page),
-                                           L, float(safety_margin))
+                                           L, POLICIES[policy], float(safety_margin))
 
     def build_into(self, out: np.ndarray) -> _abi.cb_step:
         """Schedule into `out` (a C-contiguous int32 array); returns the header. Raises on any status but OK."""

@@ -12,7 +12,8 @@ CB_DTYPE_F32, CB_DTYPE_BF16 = 0, 1
 CB_DECODING, CB_PREFILLING, CB_WAITING = 0, 1, 2
 CB_MAX_LAYERS = 2
 CB_PHASE_DECODE, CB_PHASE_ROWWISE, CB_PHASE_PREFILL, CB_PHASE_COMBINE = 1, 2, 4, 8
-ABI_VERSION = 1
+CB_POLICY_FIFO, CB_POLICY_PREFILL_FIRST = 0, 1
+ABI_VERSION = 2
 
 i32p = C.POINTER(C.c_int32)
 
@@ -29,7 +30,8 @@ class cb_layer_pool(C.Structure):
 
 class cb_sched_params(C.Structure):
     _fields_ = [("max_batch_tokens", C.c_int32), ("max_requests", C.c_int32), ("page_size", C.c_int32),
-                ("pad_page", C.c_int32), ("n_layers", C.c_int32), ("safety_margin", C.c_float)]
+                ("pad_page", C.c_int32), ("n_layers", C.c_int32), ("policy", C.c_int32),
+                ("safety_margin", C.c_float)]
 
 
 class cb_step(C.Structure):

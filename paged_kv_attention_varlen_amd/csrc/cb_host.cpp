@@ -58,6 +58,7 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
     const int32_t budget0 = params->max_batch_tokens;
     const int32_t cap = params->max_requests;
     if (P < 1 || budget0 < 1 || cap < 1 || L < 1 || L > CB_MAX_LAYERS) return CB_E_INVAL;
+    if (params->policy != CB_POLICY_FIFO && params->policy != CB_POLICY_PREFILL_FIRST) return CB_E_INVAL;
     for (int l = 0; l < L; ++l) {
         const cb_layer_pool &lay = layers[l];
         if (lay.ring_len < 0 || lay.n_free < 0 || (lay.n_free > 0 && !lay.free_pages)) return CB_E_INVAL;
@@ -93,12 +94,13 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
         return true;
     };
 
-    std::vector<Scheduled> rows;
+    std::vector<Scheduled> rows[3];   // by state: decodes, continuing prefills, admitted requests
     std::vector<int32_t> stalled;
     int32_t first_rejected = -1;
     int32_t held = 0;
     int32_t budget = budget0;
-    auto schedule = [&](int32_t i, int32_t q, const int32_t *need) {
+    auto n_rows = [&]() { return int32_t(rows[0].size() + rows[1].size() + rows[2].size()); };
+    auto schedule = [&](int32_t group, int32_t i, int32_t q, const int32_t *need) {
         Scheduled s{};
         s.req = i;
         s.q = q;
@@ -107,66 +109,86 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
             s.new_count[l] = need[l];
             taken[l] += need[l];
         }
-        rows.push_back(s);
+        rows[group].push_back(s);
         budget -= q;
     };
 
-    // 1) active decodes
-    for (int32_t i = 0; i < n_reqs; ++i) {
-        if (reqs[i].state != CB_DECODING) continue;
-        if (int32_t(rows.size()) >= cap || budget < 1) break;
-        int32_t need[CB_MAX_LAYERS];
-        pages_needed(reqs[i], 1, need);
-        if (!available(need)) {
-            stalled.push_back(i);
-            continue;
+    // active decodes, one token each
+    auto decodes = [&]() {
+        for (int32_t i = 0; i < n_reqs; ++i) {
+            if (reqs[i].state != CB_DECODING) continue;
+            if (n_rows() >= cap || budget < 1) break;
+            int32_t need[CB_MAX_LAYERS];
+            pages_needed(reqs[i], 1, need);
+            if (!available(need)) {
+                stalled.push_back(i);
+                continue;
+            }
+            schedule(0, i, 1, need);
         }
-        schedule(i, 1, need);
+    };
+    // active prefills continue where they stopped
+    auto prefills = [&]() {
+        for (int32_t i = 0; i < n_reqs; ++i) {
+            if (reqs[i].state != CB_PREFILLING) continue;
+            if (n_rows() >= cap || budget < 1) break;
+            const int32_t q = std::min(reqs[i].num_pending, budget);
+            int32_t need[CB_MAX_LAYERS];
+            pages_needed(reqs[i], q, need);
+            if (!available(need)) {
+                stalled.push_back(i);
+                continue;
+            }
+            schedule(1, i, q, need);
+        }
+    };
+    // admission of waiting requests, in arrival order
+    auto admit = [&]() {
+        for (int32_t i = 0; i < n_reqs; ++i) {
+            if (reqs[i].state != CB_WAITING) continue;
+            if (n_rows() >= cap || budget < 1) break;
+            bool low = false;
+            for (int l = 0; l < L; ++l) {
+                const cb_layer_pool &lay = layers[l];
+                if (lay.pool_pages > 0 &&
+                    double(lay.n_free - taken[l]) < double(params->safety_margin) * double(lay.pool_pages))
+                    low = true;
+            }
+            if (low) {
+                held = 1;
+                break;
+            }
+            const int32_t q = std::min(reqs[i].num_pending, budget);
+            int32_t need[CB_MAX_LAYERS];
+            pages_needed(reqs[i], q, need);
+            if (!available(need)) {
+                first_rejected = i;
+                break;
+            }
+            schedule(2, i, q, need);
+        }
+    };
+    if (params->policy == CB_POLICY_FIFO) {
+        decodes();
+        prefills();
+        admit();
+    } else {
+        prefills();
+        admit();
+        decodes();
     }
-    const int32_t num_decodes = int32_t(rows.size());
-    // 2) active prefills continue where they stopped
-    for (int32_t i = 0; i < n_reqs; ++i) {
-        if (reqs[i].state != CB_PREFILLING) continue;
-        if (int32_t(rows.size()) >= cap || budget < 1) break;
-        const int32_t q = std::min(reqs[i].num_pending, budget);
-        int32_t need[CB_MAX_LAYERS];
-        pages_needed(reqs[i], q, need);
-        if (!available(need)) {
-            stalled.push_back(i);
-            continue;
-        }
-        schedule(i, q, need);
-    }
-    // 3) admission of waiting requests, in arrival order
-    for (int32_t i = 0; i < n_reqs; ++i) {
-        if (reqs[i].state != CB_WAITING) continue;
-        if (int32_t(rows.size()) >= cap || budget < 1) break;
-        bool low = false;
-        for (int l = 0; l < L; ++l) {
-            const cb_layer_pool &lay = layers[l];
-            if (lay.pool_pages > 0 &&
-                double(lay.n_free - taken[l]) < double(params->safety_margin) * double(lay.pool_pages))
-                low = true;
-        }
-        if (low) {
-            held = 1;
-            break;
-        }
-        const int32_t q = std::min(reqs[i].num_pending, budget);
-        int32_t need[CB_MAX_LAYERS];
-        pages_needed(reqs[i], q, need);
-        if (!available(need)) {
-            first_rejected = i;
-            break;
-        }
-        schedule(i, q, need);
-    }
+    std::sort(stalled.begin(), stalled.end());
+    const int32_t num_decodes = int32_t(rows[0].size());
+    // rows laid out decodes first, then continuing prefills, then admitted requests
+    rows[0].insert(rows[0].end(), rows[1].begin(), rows[1].end());
+    rows[0].insert(rows[0].end(), rows[2].begin(), rows[2].end());
+    const std::vector<Scheduled> &all = rows[0];
 
     // ---- sizes and offsets of the packed output
-    const int32_t N = int32_t(rows.size());
+    const int32_t N = int32_t(all.size());
     int64_t T = 0;
     int32_t max_q = 0, max_seq = 0;
-    for (const Scheduled &s : rows) {
+    for (const Scheduled &s : all) {
         T += s.q;
         max_q = std::max(max_q, s.q);
         max_seq = std::max(max_seq, reqs[s.req].num_computed + s.q);
@@ -203,9 +225,9 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
     int32_t *idx = out + step->off_req_index;
     qsl[0] = 0;
     for (int32_t r = 0; r < N; ++r) {
-        qsl[r + 1] = qsl[r] + rows[r].q;
-        seq[r] = reqs[rows[r].req].num_computed + rows[r].q;
-        idx[r] = rows[r].req;
+        qsl[r + 1] = qsl[r] + all[r].q;
+        seq[r] = reqs[all[r].req].num_computed + all[r].q;
+        idx[r] = all[r].req;
     }
     std::copy(stalled.begin(), stalled.end(), out + step->off_stalled);
 
@@ -218,7 +240,7 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
         int32_t *slots = out + step->off_slot_mapping[l];
         int32_t *rlen = out + step->off_ring_len[l];
         for (int32_t r = 0; r < N; ++r) {
-            const Scheduled &s = rows[r];
+            const Scheduled &s = all[r];
             const cb_req &rq = reqs[s.req];
             int32_t *row = table + int64_t(r) * width;
             // the row's pages: those owned, then those just taken from the free list

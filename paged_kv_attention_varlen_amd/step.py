@@ -84,7 +84,8 @@ class Step:
                   "pool_pages": lay.num_pages - len(lay.padding_pages), "free_pages": lay.free_pages}
                  for lay in w.layers]
         pad = w.layers[0].padding_pages[0] if w.layers[0].padding_pages else 0
-        sched = build_metadata(w.requests, pools, w.max_batch_tokens, w.max_requests, P, w.safety_margin, pad)
+        sched = build_metadata(w.requests, pools, w.max_batch_tokens, w.max_requests, P, w.safety_margin, pad,
+                               policy=w.policy)
         if sched["status"] != 0:
             raise RuntimeError(f"cb_build_metadata returned status {sched['status']}")
         N, T = sched["num_reqs"], sched["num_tokens"]
@@ -219,7 +220,7 @@ class StepPipeline:
                  for lay in w.layers]
         pad = w.layers[0].padding_pages[0] if w.layers[0].padding_pages else 0
         self.sched = Scheduler(w.requests, pools, w.max_batch_tokens, w.max_requests, w.page_size, w.safety_margin,
-                               pad)
+                               pad, policy=w.policy)
         dt = _abi.CB_DTYPE_BF16 if w.dtype == "bf16" else _abi.CB_DTYPE_F32
         self.shapes = [_abi.cb_attn_shape(w.Hq, w.Hkv, w.D, w.page_size, dt, lay.window_left, decode_split,
                                           prefill_split) for lay in w.layers]

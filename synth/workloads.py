@@ -80,6 +80,7 @@ class Workload:
     layers: List[LayerSpec]
     requests: List[Request]
     description: str = ""
+    policy: str = "fifo"      # scheduling policy of the step: "fifo" or "prefill_first"
 
     # ------------------------------------------------------------------ values
     def values(self, tensor: str, r: int, layer: int, lo: int, hi: int) -> np.ndarray:

@@ -414,6 +414,40 @@ def check_stall_nospace_margin_cap():
     assert S.build_metadata([wt], [_layer(2, 4, 10, [])], 16, 8, P)["status"] == S.E_INVAL
 
 
+def check_prefill_first_order():
+    """PrefillFirst finishes prefill work before decodes resume (Transformers "continuous batching architecture"
+    page, section "PrefillFirst"): with a budget of 8, a decode, a continuing prefill with 6 prompt tokens left and
+    a waiting prompt of 5, FIFO runs the decode, the 6 tokens and 1 token of the new prompt; PrefillFirst runs the 6
+    tokens and 2 of the new prompt, and the decode waits for budget. Rows are laid out decodes first either way;
+    pages come from the free list in scheduling order."""
+    P = 4
+    d = Request(0, DECODING, 8, 1, [np.array([5, 6], np.int32)])          # needs a third page (a new block)
+    pf = Request(1, PREFILLING, 4, 6, [np.array([7], np.int32)])         # 4 + 6 = 10 keys -> 2 more pages
+    wt = Request(2, WAITING, 0, 5, [np.zeros(0, np.int32)])
+    free = np.arange(20, 30, dtype=np.int32)
+    s = S.build_metadata([d, pf, wt], [_layer(0, -1, 50, free)], 8, 8, P)
+    assert s["req_index"].tolist() == [0, 1, 2] and np.diff(s["query_start_loc"]).tolist() == [1, 6, 1]
+    assert s["layers"][0]["block_table"][0, :3].tolist() == [5, 6, 20]            # the decode took page 20 first
+    s = S.build_metadata([d, pf, wt], [_layer(0, -1, 50, free)], 8, 8, P, policy=S.PREFILL_FIRST)
+    assert s["req_index"].tolist() == [1, 2] and np.diff(s["query_start_loc"]).tolist() == [6, 2]
+    assert s["num_decodes"] == 0 and s["stalled"].tolist() == []
+    assert s["layers"][0]["block_table"][0, :3].tolist() == [7, 20, 21]           # the prefill took 20, 21
+    # with budget to spare the decode runs after the prefill work, laid out first, taking the next free page
+    s = S.build_metadata([d, pf, wt], [_layer(0, -1, 50, free)], 16, 8, P, policy=S.PREFILL_FIRST)
+    assert s["req_index"].tolist() == [0, 1, 2] and np.diff(s["query_start_loc"]).tolist() == [1, 6, 5]
+    assert s["layers"][0]["block_table"][0, :3].tolist() == [5, 6, 24]
+    # the safety margin holds new prompts, never the work already running (page: FIFO default 0.15)
+    s = S.build_metadata([d, pf, wt], [_layer(0, -1, 50, free[:3])], 16, 8, P, safety_margin=0.15,
+                         policy=S.PREFILL_FIRST)
+    assert s["held_by_margin"] and s["req_index"].tolist() == [0, 1]
+    s = S.build_metadata([d, pf, wt], [_layer(0, -1, 50, free[:2])], 16, 8, P, safety_margin=0.15,
+                         policy=S.PREFILL_FIRST)
+    assert s["held_by_margin"] and s["req_index"].tolist() == [1]
+    assert s["stalled"].tolist() == [0]         # the last free pages went to the prefill: the decode stalls
+    s = S.build_metadata([d, pf, wt], [_layer(0, -1, 50, free[:2])], 16, 8, P, safety_margin=0.15)
+    assert s["held_by_margin"] and s["req_index"].tolist() == [0] and s["stalled"].tolist() == [1]
+
+
 def check_four_slot_timeline():
     g = golden("four_slot_example.json")
     steps = g["decode_steps"]
@@ -467,5 +501,5 @@ ALL_CHECKS = [
     check_chunked_equals_oneshot, check_decode_equals_last_prefill_row, check_sliding_window,
     check_batch_invariance, check_workload_paged_equals_definition, check_fifo_fill_of_workloads,
     check_padding_pages_never_allocated, check_admission_all_or_nothing, check_stall_nospace_margin_cap,
-    check_four_slot_timeline,
+    check_prefill_first_order, check_four_slot_timeline,
 ]

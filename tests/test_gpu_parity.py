@@ -177,6 +177,18 @@ def test_deterministic_and_batch_invariant(torch_gpu):
     assert torch_gpu.equal(a.layers[0].out[0], c.layers[0].out[0])
 
 
+def test_prefill_first_step(torch_gpu):
+    """A step scheduled with the PrefillFirst policy (prefill work takes the budget first): every row and page against
+    the oracle, which schedules with the same policy."""
+    import dataclasses
+    for idx in (3, 5):
+        w = dataclasses.replace(make_workload(idx, mini=True), policy="prefill_first")
+        st = _run(w)
+        for l in range(len(w.layers)):
+            H.compare(w, st, l, label=f"prefill-first w{idx} layer {l}")
+            _check_pages(w, st, l)
+
+
 @pytest.mark.parametrize("mode", ["copy stream", "copy on compute stream", "concurrent prefill", "graph replay"])
 def test_pipeline_steps_match_oracle(torch_gpu, mode):
     """The benchmark's loop: steps prepared into alternating pinned/device buffers, launched with the lean path,

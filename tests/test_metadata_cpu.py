@@ -75,13 +75,43 @@ def _random_case(rng, two_layers):
     return reqs, layers, budget, cap, P, margin
 
 
+@pytest.mark.parametrize("policy", [S.FIFO, S.PREFILL_FIRST])
 @pytest.mark.parametrize("seed", range(60))
-def test_random_mixes_bit_exact(seed):
+def test_random_mixes_bit_exact(seed, policy):
     rng = np.random.default_rng(seed)
     reqs, layers, budget, cap, P, margin = _random_case(rng, two_layers=bool(seed % 2))
-    ref = S.build_metadata(reqs, layers, budget, cap, P, margin, 0)
-    got = cb.build_metadata(reqs, layers, budget, cap, P, margin, 0)
+    ref = S.build_metadata(reqs, layers, budget, cap, P, margin, 0, policy=policy)
+    got = cb.build_metadata(reqs, layers, budget, cap, P, margin, 0, policy=policy)
     _compare(ref, got)
+
+
+@pytest.mark.parametrize("idx", [3, 5])
+def test_workload_prefill_first_bit_exact(idx):
+    w = make_workload(idx)
+    pad = w.layers[0].padding_pages[0] if w.layers[0].padding_pages else 0
+    ref = S.build_metadata(w.requests, _pools(w), w.max_batch_tokens, w.max_requests, w.page_size, 0.0, pad,
+                           policy=S.PREFILL_FIRST)
+    got = cb.build_metadata(w.requests, _pools(w), w.max_batch_tokens, w.max_requests, w.page_size, 0.0, pad,
+                            policy="prefill_first")
+    _compare(ref, got)
+    # the chunks get the budget first: every prompt token that fits is scheduled before any decode
+    pre = int(np.diff(ref["query_start_loc"])[ref["num_decodes"]:].sum())
+    assert pre == min(w.max_batch_tokens, sum(rq.num_pending for rq in w.requests if rq.state != DECODING))
+
+
+def test_unknown_policy_is_rejected():
+    lay = [{"ring_len": 0, "window_left": -1, "pool_pages": 10, "free_pages": np.arange(2, 12)}]
+    ok = [Request(0, WAITING, 0, 3, [np.zeros(0, np.int32)])]
+    assert S.build_metadata(ok, lay, 16, 8, 4, policy="lifo")["status"] == S.E_INVAL
+    lib = cb._abi.load()
+    params = cb._abi.cb_sched_params(16, 8, 4, 0, 1, 7, 0.0)
+    pools = (cb._abi.cb_layer_pool * 1)(cb._abi.cb_layer_pool(0, -1, 10, 0, None))
+    step = cb._abi.cb_step()
+    buf = np.zeros(64, np.int32)
+    reqs = (cb._abi.cb_req * 1)()
+    st = lib.cb_build_metadata(reqs, 0, cb.C.byref(params), pools, buf.ctypes.data_as(cb._abi.i32p), 64,
+                               cb.C.byref(step))
+    assert st == cb._abi.CB_E_INVAL
 
 
 def test_error_paths_match():
