@@ -87,6 +87,48 @@ def stored_traffic():
         return None
 
 
+def measure_swap(step, n_pages: int, reps: int = 5) -> dict:
+    """Offloading round trip of n_pages distinct pages of the first layer (K and V): the gather kernel into a device
+    staging buffer, the copy to pinned host memory, the copy back, and the scatter kernel into other pages. HIP events
+    on the stream that runs them; bytes are the pages' bytes (the kernels read and write each once)."""
+    import torch
+    from paged_kv_attention_varlen_amd import copy_pages
+    from paged_kv_attention_varlen_amd.swap import HostSwap
+    L = step.layers[0]
+    n_pages = min(n_pages, L.k_cache.shape[0] // 2)
+    perm = torch.randperm(L.k_cache.shape[0], device="cuda").to(torch.int32)
+    src, dst = perm[:n_pages].contiguous(), perm[n_pages:2 * n_pages].contiguous()
+    pool = HostSwap(L.k_cache, L.v_cache, n_pages)
+    page_bytes = (L.k_cache[0].numel() + L.v_cache[0].numel()) * L.k_cache.element_size()
+    total = n_pages * page_bytes
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    t = {"gather": [], "to_host": [], "to_device": [], "scatter": []}
+    for _ in range(reps + 1):
+        ev[0].record()
+        copy_pages(pool.stage_k, L.k_cache, None, src)
+        copy_pages(pool.stage_v, L.v_cache, None, src)
+        ev[1].record()
+        pool.host_k.copy_(pool.stage_k, non_blocking=True)
+        pool.host_v.copy_(pool.stage_v, non_blocking=True)
+        ev[2].record()
+        pool.stage_k.copy_(pool.host_k, non_blocking=True)
+        pool.stage_v.copy_(pool.host_v, non_blocking=True)
+        ev[3].record()
+        copy_pages(L.k_cache, pool.stage_k, dst, None)
+        copy_pages(L.v_cache, pool.stage_v, dst, None)
+        ev[4].record()
+        torch.cuda.synchronize()
+        for k, (a, b) in zip(t, ((0, 1), (1, 2), (2, 3), (3, 4))):
+            t[k].append(ev[a].elapsed_time(ev[b]))
+    us = {k: float(np.median(v[1:])) * 1e3 for k, v in t.items()}
+    return {"pages": n_pages, "bytes": total, "page_bytes": page_bytes,
+            "us": {k: round(v, 1) for k, v in us.items()},
+            "gb_per_s": {"gather (HBM read + write)": round(2 * total / (us["gather"] / 1e6) / 1e9, 1),
+                         "device to pinned host": round(total / (us["to_host"] / 1e6) / 1e9, 1),
+                         "pinned host to device": round(total / (us["to_device"] / 1e6) / 1e9, 1),
+                         "scatter (HBM read + write)": round(2 * total / (us["scatter"] / 1e6) / 1e9, 1)}}
+
+
 def cpu_baseline(w, sched, seconds: float):
     """Time the oracle (as it stands) on a bounded sample of the step's query rows: all decode rows first, then
     prefill rows in random order, until `seconds` of oracle time (repeating the step if it finishes sooner). Input
@@ -147,6 +189,9 @@ def main():
     ap.add_argument("--graphs", action="store_true",
                     help="replay each step's kernels as a captured HIP graph (steps that carry timing events run "
                          "eagerly)")
+    ap.add_argument("--swap-pages", type=int, default=0,
+                    help="also measure offloading N cache pages of the first layer to pinned host memory and back "
+                         "(gather kernel, device-to-host copy, host-to-device copy, scatter kernel)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, run a plain device copy of this many MiB three times (untimed), the "
                          "known-size reference for scaling HBM byte counters")
@@ -270,6 +315,8 @@ def main():
     }
     if copy_ref:
         line["device_copy_reference"] = copy_ref
+    if args.swap_pages:
+        line["kv_swap"] = measure_swap(step, args.swap_pages)
     print(json.dumps(line), flush=True)
 
 

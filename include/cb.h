@@ -197,6 +197,24 @@ cb_status cb_kv_append(void *k_cache, void *v_cache, const void *k_new, const vo
                        const int32_t *d_slot_mapping, int32_t num_tokens, int32_t num_pages, int32_t page_size,
                        int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void *stream);
 
+/* -------------------------------------------------------------------------------------------- cb_kv_copy_pages */
+
+/*
+ * Copy whole pages between two page arrays on the device: page i goes from src + src_pages[i] * page_bytes to
+ * dst + dst_pages[i] * page_bytes (a NULL list stands for 0, 1, ..., n-1). With a contiguous device buffer on one
+ * side this is the batched gather / scatter of a request's cache pages that swapping to host memory needs
+ * (Transformers "continuous batching architecture" page, section "Offloading": the KV blocks of offloaded requests
+ * are copied to a pre-allocated pinned CPU buffer in one transfer, and copied back when GPU cache space frees up);
+ * the transfer between that buffer and pinned host memory is an ordinary asynchronous copy. Call once for the K
+ * tensor and once for the V tensor: a page is Hkv * page_size * head_dim elements in either layout.
+ * Device pointers: dst, src, d_dst_pages [n], d_src_pages [n]; dst_slots / src_slots are the pages each array holds.
+ * Pairs with an index outside its array are skipped. Pages of src and dst must not overlap. Async on `stream`.
+ * Returns CB_OK, CB_E_INVAL (negative sizes, page_bytes not a multiple of 16, null buffers, n above an array without
+ * an index list), CB_E_UNSUPPORTED (page_bytes above 1 GiB) or CB_E_HIP.
+ */
+cb_status cb_kv_copy_pages(void *dst, const int32_t *d_dst_pages, int32_t dst_slots, const void *src,
+                           const int32_t *d_src_pages, int32_t src_slots, int32_t n, int64_t page_bytes, void *stream);
+
 /* ------------------------------------------------------------------------------------------ cb_paged_attention */
 
 typedef struct cb_attn_args {

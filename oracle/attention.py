@@ -147,6 +147,19 @@ def kv_append(k_cache, v_cache, k_new, v_new, slot_mapping, page_size: int):
         v_cache[page, off] = v_new[t]
 
 
+def copy_pages(dst, dst_pages, src, src_pages):
+    """Whole-page copies: page i goes from src[src_pages[i]] to dst[dst_pages[i]] (None stands for i). Pairs with an
+    index outside its array are skipped. This is the offloading copy of the Transformers "continuous batching
+    architecture" page (section "Offloading"): a request's KV blocks moved to a swap buffer and back, unchanged."""
+    n = len(src_pages) if src_pages is not None else (len(dst_pages) if dst_pages is not None
+                                                     else min(len(dst), len(src)))
+    for i in range(n):
+        sp = int(src_pages[i]) if src_pages is not None else i
+        dp = int(dst_pages[i]) if dst_pages is not None else i
+        if 0 <= sp < len(src) and 0 <= dp < len(dst):
+            dst[dp] = src[sp]
+
+
 def paged_attention(q, k_cache, v_cache, query_start_loc, seq_lens, block_table, page_size: int, scale: float,
                     window_left: int = -1, ring_len=None, rows=None):
     """Attention of every query row of a ragged step, reading K/V through the block table (or ring).

@@ -246,6 +246,31 @@ def kv_append(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None) -> None
         raise CbError(st, "cb_kv_append")
 
 
+def copy_pages(dst, src, dst_pages=None, src_pages=None, stream=None) -> None:
+    """cb_kv_copy_pages: page i of the copy goes from src[src_pages[i]] to dst[dst_pages[i]] (None: page i).
+    dst, src: contiguous device tensors whose first dimension counts pages (a cache tensor, or a swap buffer of
+    the same page shape); dst_pages / src_pages: int32 device tensors of equal length, or None."""
+    lib = _abi.load()
+    for t, nm in ((dst, "dst"), (src, "src")):
+        _check_dev(t, nm)
+    if tuple(dst.shape[1:]) != tuple(src.shape[1:]) or dst.dtype != src.dtype:
+        raise ValueError("dst and src must hold pages of the same shape and dtype")
+    lists = [x for x in (dst_pages, src_pages) if x is not None]
+    for x in lists:
+        _check_dev(x, "page list")
+        if str(x.dtype) != "torch.int32":
+            raise ValueError("page lists must be int32")
+    if len({x.numel() for x in lists}) > 1:
+        raise ValueError("page lists differ in length")
+    n = lists[0].numel() if lists else min(dst.shape[0], src.shape[0])
+    page_bytes = (dst[0].numel() if dst.shape[0] else src[0].numel()) * dst.element_size()
+    st = lib.cb_kv_copy_pages(dst.data_ptr(), dst_pages.data_ptr() if dst_pages is not None else None, dst.shape[0],
+                              src.data_ptr(), src_pages.data_ptr() if src_pages is not None else None, src.shape[0],
+                              n, page_bytes, _stream(stream))
+    if st != CB_OK:
+        raise CbError(st, "cb_kv_copy_pages")
+
+
 def _args(out, q, k_cache, v_cache, block_table, plan: AttnPlan, plan_dev, scale, workspace, phases=0):
     a = _abi.cb_attn_args()
     a.out, a.q = out.data_ptr(), q.data_ptr()

@@ -67,7 +67,7 @@ class cb_attn_args(C.Structure):
                 ("phases", C.c_int32)]
 
 
-EXPORTS = ("cb_build_metadata", "cb_plan_attention", "cb_kv_append", "cb_paged_attention",
+EXPORTS = ("cb_build_metadata", "cb_plan_attention", "cb_kv_append", "cb_kv_copy_pages", "cb_paged_attention",
            "cb_paged_attention_workspace_size", "cb_status_str", "cb_abi_version")
 
 _lib = None
@@ -97,6 +97,9 @@ def load(path: str = LIB_PATH):
     lib.cb_kv_append.restype = C.c_int32
     lib.cb_kv_append.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
                                  C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
+    lib.cb_kv_copy_pages.restype = C.c_int32
+    lib.cb_kv_copy_pages.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                                     C.c_int64, C.c_void_p]
     lib.cb_paged_attention.restype = C.c_int32
     lib.cb_paged_attention.argtypes = [C.POINTER(cb_attn_args), C.c_void_p]
     lib.cb_paged_attention_workspace_size.restype = C.c_size_t

@@ -161,6 +161,36 @@ __global__ __launch_bounds__(128) void kv_append_kernel(T *__restrict__ kc, T *_
     }
 }
 
+// ============================================================================================ page copies
+//
+// Whole pages between two page arrays (cache <-> contiguous swap buffer, or cache <-> cache): page i goes from
+// src[src_pages[i]] to dst[dst_pages[i]] (a null list means page i itself). One work group per (page, 16 KB piece);
+// every thread moves four 16-byte chunks with streaming loads. Pairs with an index outside its array are skipped.
+
+constexpr int kCopyPiece = 16384;   // bytes per work group
+
+__global__ __launch_bounds__(256) void copy_pages_kernel(uint8_t *__restrict__ dst, const int32_t *__restrict__ dst_pages,
+                                                         int dst_slots, const uint8_t *__restrict__ src,
+                                                         const int32_t *__restrict__ src_pages, int src_slots,
+                                                         int64_t page_bytes) {
+    const int i = blockIdx.x;
+    const int sp = src_pages ? src_pages[i] : i;
+    const int dp = dst_pages ? dst_pages[i] : i;
+    if (sp < 0 || sp >= src_slots || dp < 0 || dp >= dst_slots) return;
+    const int64_t lo = int64_t(blockIdx.y) * kCopyPiece;
+    const int64_t hi = min(page_bytes, lo + kCopyPiece);
+    const uint8_t *s = src + int64_t(sp) * page_bytes;
+    uint8_t *d = dst + int64_t(dp) * page_bytes;
+    u32x4 v[4];
+    int64_t o = lo + 16 * threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (o + 4096 * k < hi) v[k] = load16_stream(s + o + 4096 * k);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (o + 4096 * k < hi) store16(d + o + 4096 * k, v[k]);
+}
+
 // ===================================================================== split-KV decode (bf16, MFMA 16x16x32)
 //
 // Work group = one (decode row split, kv head); 4 waves take the split's 32-key tiles round-robin and merge their
@@ -928,6 +958,23 @@ extern "C" cb_status cb_kv_append(void *k_cache, void *v_cache, const void *k_ne
                            static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new),
                            d_slot_mapping, num_tokens, num_pages, page_size, num_kv_heads, head_dim);
     }
+    return hipGetLastError() == hipSuccess ? CB_OK : CB_E_HIP;
+}
+
+extern "C" cb_status cb_kv_copy_pages(void *dst, const int32_t *d_dst_pages, int32_t dst_slots, const void *src,
+                                      const int32_t *d_src_pages, int32_t src_slots, int32_t n, int64_t page_bytes,
+                                      void *stream) {
+    if (n < 0 || dst_slots < 0 || src_slots < 0 || page_bytes < 16 || page_bytes % 16 != 0) return CB_E_INVAL;
+    if (n == 0) return CB_OK;
+    if (!dst || !src) return CB_E_INVAL;
+    if (!d_dst_pages && n > dst_slots) return CB_E_INVAL;
+    if (!d_src_pages && n > src_slots) return CB_E_INVAL;
+    const int64_t pieces = (page_bytes + kCopyPiece - 1) / kCopyPiece;
+    if (pieces > 65535) return CB_E_UNSUPPORTED;
+    const dim3 grid{static_cast<unsigned>(n), static_cast<unsigned>(pieces), 1u};
+    hipLaunchKernelGGL(copy_pages_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint8_t *>(dst), d_dst_pages, dst_slots, static_cast<const uint8_t *>(src),
+                       d_src_pages, src_slots, page_bytes);
     return hipGetLastError() == hipSuccess ? CB_OK : CB_E_HIP;
 }
 

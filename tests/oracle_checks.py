@@ -448,6 +448,38 @@ def check_prefill_first_order():
     assert s["held_by_margin"] and s["req_index"].tolist() == [0] and s["stalled"].tolist() == [1]
 
 
+def check_swap_roundtrip_preserves_attention():
+    """Offloading moves a request's pages to a swap buffer and back into other free pages; with the block table
+    pointing at the new pages, every output row is unchanged (attention depends on the pages' contents only through
+    the block table)."""
+    rng = np.random.default_rng(11)
+    P, Hq, Hkv, D, n_pages = 4, 4, 2, 8, 24
+    qsl = np.array([0, 1, 4], np.int32)
+    seq = np.array([11, 9], np.int32)
+    table = np.array([[5, 9, 2], [7, 3, 14]], np.int32)
+    kc = rng.standard_normal((n_pages, P, Hkv, D))
+    vc = rng.standard_normal((n_pages, P, Hkv, D))
+    q = rng.standard_normal((4, Hq, D))
+    before = A.paged_attention(q, kc, vc, qsl, seq, table, P, 0.3)
+    swap_k = np.zeros((3, P, Hkv, D))
+    swap_v = np.zeros((3, P, Hkv, D))
+    A.copy_pages(swap_k, None, kc, table[1])
+    A.copy_pages(swap_v, None, vc, table[1])
+    kc[table[1]] = np.nan                        # the freed pages are reused by someone else
+    vc[table[1]] = np.nan
+    new = np.array([20, 16, 18], np.int32)
+    A.copy_pages(kc, new, swap_k, None)
+    A.copy_pages(vc, new, swap_v, None)
+    table2 = table.copy()
+    table2[1] = new
+    after = A.paged_attention(q, kc, vc, qsl, seq, table2, P, 0.3)
+    assert np.array_equal(before, after)
+    # out-of-range pairs are skipped, the rest copied
+    dst = np.zeros((2, 3))
+    A.copy_pages(dst, np.array([1, 5]), np.arange(9.0).reshape(3, 3), np.array([2, 0]))
+    assert dst.tolist() == [[0, 0, 0], [6, 7, 8]]
+
+
 def check_four_slot_timeline():
     g = golden("four_slot_example.json")
     steps = g["decode_steps"]
@@ -501,5 +533,5 @@ ALL_CHECKS = [
     check_chunked_equals_oneshot, check_decode_equals_last_prefill_row, check_sliding_window,
     check_batch_invariance, check_workload_paged_equals_definition, check_fifo_fill_of_workloads,
     check_padding_pages_never_allocated, check_admission_all_or_nothing, check_stall_nospace_margin_cap,
-    check_prefill_first_order, check_four_slot_timeline,
+    check_prefill_first_order, check_swap_roundtrip_preserves_attention, check_four_slot_timeline,
 ]

@@ -78,3 +78,10 @@ def test_device_calls_reject_bad_arguments_without_launching():
     assert lib.cb_paged_attention(C.byref(a), None) == _abi.CB_E_INVAL     # null pointers
     a.phases = 99
     assert lib.cb_paged_attention(C.byref(a), None) == _abi.CB_E_INVAL
+    # page copies: sizes checked before any launch
+    assert lib.cb_kv_copy_pages(None, None, 4, None, None, 4, 0, 4096, None) == _abi.CB_OK      # nothing to copy
+    assert lib.cb_kv_copy_pages(None, None, 4, None, None, 4, -1, 4096, None) == _abi.CB_E_INVAL
+    assert lib.cb_kv_copy_pages(None, None, 4, None, None, 4, 2, 4100, None) == _abi.CB_E_INVAL  # not 16-aligned
+    assert lib.cb_kv_copy_pages(None, None, 4, None, None, 4, 2, 4096, None) == _abi.CB_E_INVAL  # null buffers
+    assert lib.cb_kv_copy_pages(1, None, 4, 1, None, 8, 6, 4096, None) == _abi.CB_E_INVAL        # 6 pages > 4 slots
+    assert lib.cb_kv_copy_pages(1, None, 8, 1, None, 8, 2, 1 << 40, None) == _abi.CB_E_UNSUPPORTED

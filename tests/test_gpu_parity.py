@@ -211,3 +211,65 @@ def test_pipeline_steps_match_oracle(torch_gpu, mode):
                 H.compare(w, st, l, label=f"pipeline {mode} w{idx} layer {l} repetition {rep}")
         if mode == "graph replay":
             assert len(pipe.graphs) == 2, "one graph per metadata buffer"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_copy_pages_bit_exact(torch_gpu, dtype):
+    """cb_kv_copy_pages against the oracle's page copy: random page lists (some out of range, skipped), both
+    directions (cache -> swap buffer with a source list, swap buffer -> cache with a destination list)."""
+    import paged_kv_attention_varlen_amd as cb
+    torch = torch_gpu
+    rng = np.random.default_rng(3)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    n_pages, n_swap = 40, 12
+    for shape in ((8, 16, 128), (8, 128, 16), (2, 4, 64)):           # K page, V^T page, a small page
+        cache = torch.randn((n_pages,) + shape, device="cuda").to(tdt)
+        swap = torch.full((n_swap,) + shape, float("nan"), device="cuda").to(tdt)
+        src = rng.permutation(n_pages)[:n_swap].astype(np.int32)
+        src[3] = n_pages + 5                                           # out of range: skipped
+        cb.copy_pages(swap, cache, None, torch.from_numpy(src).cuda())
+        ref = np.full((n_swap,) + shape, np.nan, np.float32)
+        A.copy_pages(ref, None, cache.float().cpu().numpy(), src)
+        torch.cuda.synchronize()
+        assert H.same_bits(swap.float().cpu().numpy(), ref)
+        dst = rng.permutation(n_pages)[:n_swap].astype(np.int32)
+        dst[0] = -1                                                    # skipped
+        before = cache.float().cpu().numpy()
+        cb.copy_pages(cache, swap, torch.from_numpy(dst).cuda(), None)
+        ref = before.copy()
+        A.copy_pages(ref, dst, swap.float().cpu().numpy(), None)
+        torch.cuda.synchronize()
+        assert H.same_bits(cache.float().cpu().numpy(), ref)
+
+
+def test_swap_out_and_back_preserves_outputs(torch_gpu):
+    """Offloading round trip through pinned host memory: a request's pages go out, the freed pages are poisoned,
+    the request comes back into other free pages with its block-table row updated, and the step's attention output
+    is bitwise what it was."""
+    import torch
+    from paged_kv_attention_varlen_amd.swap import HostSwap
+    w = make_workload(3, mini=True)
+    st = _run(w)
+    L = st.layers[0]
+    before = L.out.clone()
+    sched = st.sched
+    P = w.page_size
+    used = sched["layers"][0]["used_pages"]
+    spare = list(np.asarray(w.layers[0].free_pages[used:], np.int32))   # pages no row of the step holds
+    for r in (0, sched["num_reqs"] - 2):                               # a decode row and a prefill row
+        n = -(-int(sched["seq_lens"][r]) // P)
+        old = L.block_table[r, :n].clone()
+        assert len(spare) >= n, "workload pool has no spare pages for the test"
+        new = torch.from_numpy(np.array([spare.pop() for _ in range(n)], np.int32)).cuda()
+        pool = HostSwap(L.k_cache, L.v_cache, capacity=n)
+        pool.swap_out(L.k_cache, L.v_cache, old)
+        torch.cuda.synchronize()
+        L.k_cache[old.long()] = float("nan")
+        L.v_cache[old.long()] = float("nan")
+        pool.swap_in(L.k_cache, L.v_cache, new)
+        L.block_table[r, :n] = new
+        L.out.fill_(float("nan"))
+        st.attend(0)
+        torch.cuda.synchronize()
+        print(f"[gpu] swap round trip of row {r}: {n} pages", flush=True)
+        assert torch.equal(L.out, before)
