@@ -253,6 +253,57 @@ size_t cb_paged_attention_workspace_size(const cb_attn_args *args);
  */
 cb_status cb_paged_attention(const cb_attn_args *args, void *stream);
 
+/* ------------------------------------------------------------------------------------------------ prefix cache */
+
+/*
+ * Page sharing between requests with a common prompt prefix (Transformers "continuous batching architecture" page,
+ * sections "前缀缓存" (prefix cache) and "驱逐" (eviction)): every full block of a prompt gets a content hash; a later
+ * request whose leading blocks are cached reuses their pages and skips their prefill; shared pages carry reference
+ * counts and return to a free list only when the last holder releases them; a freed page that holds a hashed block
+ * keeps it ("initialized") for later matches, until fresh pages run out and the most recently freed one is demoted
+ * (its hash dropped). Host only, deterministic; page ids are the caller's pool (full-attention layers: the page says
+ * sliding and hybrid models do not share). All functions return CB_E_INVAL on null or out-of-range arguments.
+ */
+typedef struct cb_prefix_cache cb_prefix_cache;   /* opaque, owned by the library between create and destroy */
+
+/* FNV-1a 64-bit hash of n bytes (offset basis 14695981039346656037, prime 1099511628211). */
+uint64_t cb_fnv1a64(const void *data, int64_t n);
+
+/* Chain hashes of the n_tokens / page_size full blocks of a token sequence: block b hashes, with FNV-1a 64, the
+ * 8 little-endian bytes of block b-1's hash (the FNV offset basis for b = 0) followed by the block's token ids as
+ * 4 little-endian bytes each. out: [n_tokens / page_size] (caller-owned). */
+cb_status cb_block_hashes(const int32_t *tokens, int32_t n_tokens, int32_t page_size, uint64_t *out);
+
+/* A cache over pages 0 .. num_pages-1, of which free_pages (distinct, in allocation order) start free and empty.
+ * Returns CB_E_CAPACITY if the host allocation of the bookkeeping fails. */
+cb_status cb_pcache_create(int32_t num_pages, const int32_t *free_pages, int32_t n_free, cb_prefix_cache **out);
+void cb_pcache_destroy(cb_prefix_cache *cache);
+
+/* Longest cached prefix: the leading blocks whose hashes are registered. Their pages go to pages_out [n_blocks] and
+ * each gains a reference (a freed one comes back into use); *n_matched tells how many. */
+cb_status cb_pcache_match(cb_prefix_cache *cache, const uint64_t *hashes, int32_t n_blocks, int32_t *pages_out,
+                          int32_t *n_matched);
+
+/* n fresh pages with one reference each, into pages_out [n]: empty pages first, in free-list order, then demoted
+ * initialized pages, most recently freed first. All or nothing: CB_E_NOSPACE, and nothing taken, if fewer exist. */
+cb_status cb_pcache_allocate(cb_prefix_cache *cache, int32_t n, int32_t *pages_out);
+
+/* Page `page` (held, not yet registered) now holds the full block with this hash: register it. If another page
+ * already holds that block, this page stays unregistered (private). */
+cb_status cb_pcache_commit(cb_prefix_cache *cache, int32_t page, uint64_t hash);
+
+/* Drop one reference per entry of pages [n] (a page may appear as often as references are held; the whole call is
+ * checked first). A page left with none becomes free: initialized if it holds a registered block, empty otherwise. */
+cb_status cb_pcache_release(cb_prefix_cache *cache, const int32_t *pages, int32_t n);
+
+/* Counts: empty free pages, initialized free pages, registered blocks. */
+cb_status cb_pcache_stats(const cb_prefix_cache *cache, int32_t *n_empty, int32_t *n_initialized_free,
+                          int32_t *n_registered);
+
+/* One page's references, whether it holds a registered block, and that block's hash (0 if none). */
+cb_status cb_pcache_page_info(const cb_prefix_cache *cache, int32_t page, int32_t *refs, int32_t *registered,
+                              uint64_t *hash);
+
 /* --------------------------------------------------------------------------------------------------- utilities */
 
 const char *cb_status_str(cb_status status);

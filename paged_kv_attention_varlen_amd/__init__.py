@@ -271,6 +271,72 @@ def copy_pages(dst, src, dst_pages=None, src_pages=None, stream=None) -> None:
         raise CbError(st, "cb_kv_copy_pages")
 
 
+# ------------------------------------------------------------------------------------------------ prefix cache
+
+def block_hashes(tokens, page_size: int) -> np.ndarray:
+    """cb_block_hashes: chain hashes (uint64) of the full blocks of a token sequence."""
+    t = _i32(tokens)
+    out = np.zeros(max(t.size // page_size, 1), dtype=np.uint64)
+    st = _abi.load().cb_block_hashes(_ptr(t), t.size, int(page_size), out.ctypes.data_as(C.POINTER(C.c_uint64)))
+    if st != CB_OK:
+        raise CbError(st, "cb_block_hashes")
+    return out[:t.size // page_size]
+
+
+class PrefixCache:
+    """The library's prefix cache (cb_pcache_*): page sharing by block hash with reference counts and lazy
+    demotion of freed blocks. Page lists in and out are int32 numpy arrays."""
+
+    def __init__(self, num_pages: int, free_pages):
+        self._lib = _abi.load()
+        f = _i32(free_pages)
+        h = C.c_void_p()
+        st = self._lib.cb_pcache_create(int(num_pages), _ptr(f), f.size, C.byref(h))
+        if st != CB_OK:
+            raise CbError(st, "cb_pcache_create")
+        self._h = h
+
+    def __del__(self):
+        if getattr(self, "_h", None) and self._h.value:
+            self._lib.cb_pcache_destroy(self._h)
+            self._h = None
+
+    def _call(self, st, what):
+        if st != CB_OK:
+            raise CbError(st, what)
+
+    def match(self, hashes) -> np.ndarray:
+        hs = np.ascontiguousarray(np.asarray(hashes, dtype=np.uint64))
+        out = np.zeros(max(hs.size, 1), dtype=np.int32)
+        n = C.c_int32()
+        self._call(self._lib.cb_pcache_match(self._h, hs.ctypes.data_as(C.POINTER(C.c_uint64)), hs.size, _ptr(out),
+                                             C.byref(n)), "cb_pcache_match")
+        return out[:n.value].copy()
+
+    def allocate(self, n: int) -> np.ndarray:
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        self._call(self._lib.cb_pcache_allocate(self._h, int(n), _ptr(out)), "cb_pcache_allocate")
+        return out[:n].copy()
+
+    def commit(self, page: int, h) -> None:
+        self._call(self._lib.cb_pcache_commit(self._h, int(page), int(h)), "cb_pcache_commit")
+
+    def release(self, pages) -> None:
+        p = _i32(pages)
+        self._call(self._lib.cb_pcache_release(self._h, _ptr(p), p.size), "cb_pcache_release")
+
+    def stats(self):
+        a, b, c = C.c_int32(), C.c_int32(), C.c_int32()
+        self._call(self._lib.cb_pcache_stats(self._h, C.byref(a), C.byref(b), C.byref(c)), "cb_pcache_stats")
+        return a.value, b.value, c.value
+
+    def page_info(self, page: int):
+        r, reg, h = C.c_int32(), C.c_int32(), C.c_uint64()
+        self._call(self._lib.cb_pcache_page_info(self._h, int(page), C.byref(r), C.byref(reg), C.byref(h)),
+                   "cb_pcache_page_info")
+        return r.value, bool(reg.value), h.value
+
+
 def _args(out, q, k_cache, v_cache, block_table, plan: AttnPlan, plan_dev, scale, workspace, phases=0):
     a = _abi.cb_attn_args()
     a.out, a.q = out.data_ptr(), q.data_ptr()

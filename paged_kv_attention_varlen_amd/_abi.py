@@ -68,7 +68,9 @@ class cb_attn_args(C.Structure):
 
 
 EXPORTS = ("cb_build_metadata", "cb_plan_attention", "cb_kv_append", "cb_kv_copy_pages", "cb_paged_attention",
-           "cb_paged_attention_workspace_size", "cb_status_str", "cb_abi_version")
+           "cb_paged_attention_workspace_size", "cb_fnv1a64", "cb_block_hashes", "cb_pcache_create",
+           "cb_pcache_destroy", "cb_pcache_match", "cb_pcache_allocate", "cb_pcache_commit", "cb_pcache_release",
+           "cb_pcache_stats", "cb_pcache_page_info", "cb_status_str", "cb_abi_version")
 
 _lib = None
 
@@ -104,6 +106,27 @@ def load(path: str = LIB_PATH):
     lib.cb_paged_attention.argtypes = [C.POINTER(cb_attn_args), C.c_void_p]
     lib.cb_paged_attention_workspace_size.restype = C.c_size_t
     lib.cb_paged_attention_workspace_size.argtypes = [C.POINTER(cb_attn_args)]
+    u64p = C.POINTER(C.c_uint64)
+    lib.cb_fnv1a64.restype = C.c_uint64
+    lib.cb_fnv1a64.argtypes = [C.c_void_p, C.c_int64]
+    lib.cb_block_hashes.restype = C.c_int32
+    lib.cb_block_hashes.argtypes = [i32p, C.c_int32, C.c_int32, u64p]
+    lib.cb_pcache_create.restype = C.c_int32
+    lib.cb_pcache_create.argtypes = [C.c_int32, i32p, C.c_int32, C.POINTER(C.c_void_p)]
+    lib.cb_pcache_destroy.restype = None
+    lib.cb_pcache_destroy.argtypes = [C.c_void_p]
+    lib.cb_pcache_match.restype = C.c_int32
+    lib.cb_pcache_match.argtypes = [C.c_void_p, u64p, C.c_int32, i32p, i32p]
+    lib.cb_pcache_allocate.restype = C.c_int32
+    lib.cb_pcache_allocate.argtypes = [C.c_void_p, C.c_int32, i32p]
+    lib.cb_pcache_commit.restype = C.c_int32
+    lib.cb_pcache_commit.argtypes = [C.c_void_p, C.c_int32, C.c_uint64]
+    lib.cb_pcache_release.restype = C.c_int32
+    lib.cb_pcache_release.argtypes = [C.c_void_p, i32p, C.c_int32]
+    lib.cb_pcache_stats.restype = C.c_int32
+    lib.cb_pcache_stats.argtypes = [C.c_void_p, i32p, i32p, i32p]
+    lib.cb_pcache_page_info.restype = C.c_int32
+    lib.cb_pcache_page_info.argtypes = [C.c_void_p, C.c_int32, i32p, i32p, u64p]
     lib.cb_status_str.restype = C.c_char_p
     lib.cb_status_str.argtypes = [C.c_int32]
     lib.cb_abi_version.restype = C.c_int32

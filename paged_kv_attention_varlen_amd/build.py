@@ -50,8 +50,10 @@ def build(verbose: bool = False) -> str:
     logs.append(_run([hipcc, f"--offload-arch={ARCH}", *DEVICE_FLAGS, *common, "-c",
                       os.path.join(CSRC, "cb_device.hip"), "-o", dev_o]))
     logs.append(_run([hipcc, "-x", "c++", *common, "-c", os.path.join(CSRC, "cb_host.cpp"), "-o", host_o]))
+    prefix_o = os.path.join(bdir, "cb_prefix.o")
+    logs.append(_run([hipcc, "-x", "c++", *common, "-c", os.path.join(CSRC, "cb_prefix.cpp"), "-o", prefix_o]))
     tmp = LIB + ".tmp"
-    logs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", dev_o, host_o, "-o", tmp]))
+    logs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", dev_o, host_o, prefix_o, "-o", tmp]))
     os.replace(tmp, LIB)
     if verbose:
         print("\n".join(x for x in logs if x.strip()))

@@ -543,14 +543,15 @@ __global__ __launch_bounds__(64) void rowwise_kernel(const T *__restrict__ q, T 
 // Per tile, with the next tile's copies in flight (double buffering):
 //   QK(half 0) | QK(half 1) beside softmax(half 0) | PV(half 0) beside softmax(half 1) | PV(half 1)
 // Softmax in the log2 domain with a lazily moved running maximum: the weights are computed speculatively against the
-// current maximum, and only when some row's tile maximum exceeds it by more than kRescaleSlack does a rare path move
+// current maximum, and only when some row's weights could exceed 2^8 (its sum does) does a rare path move
 // it, rescale that row's accumulators and recompute the weights. Tiles every row sees completely skip the mask.
 
 constexpr int kPfRows = 128;   // query rows of one work group: 4 waves x 32
 constexpr int kPfKeys = 64;    // keys per tile
 constexpr int kPrefillMaxPages = 1536;   // page ids of one prefill item staged in LDS (split / page + 2)
-constexpr float kRescaleSlack = 8.f;     // log2 units the running maximum may lag behind the true one
-constexpr float kWeightSumBound = 256.f; // 2^kRescaleSlack: a half's weight sum above it sends the row to the rare path
+// the running maximum may lag 8 (log2 units) behind the true one: a half's weight sum above 2^8 sends the row to the
+// rare path
+constexpr float kWeightSumBound = 256.f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -751,7 +752,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         };
         // Softmax of one half against the current running maximum (speculative): the bf16 weights (the B operands
         // of the PV product) and their sum. The weights are trusted when the row already has a maximum and their sum
-        // stays below 2^kRescaleSlack, which bounds every weight; otherwise (first visible keys of the row, or scores
+        // stays below kWeightSumBound, which bounds every weight; otherwise (first visible keys of the row, or scores
         // that climbed past the running maximum) the rare path below settles the row. No row maximum is computed on
         // the common path.
         auto softmax_half = [&](const f32x16 &S, bf16x8 (&pf)[2], float &lsum) {

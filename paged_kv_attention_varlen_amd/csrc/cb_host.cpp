@@ -313,7 +313,7 @@ extern "C" cb_status cb_plan_attention(const int32_t *qsl, const int32_t *seq_le
 
     // ---- split sizes. Decode: enough (row, split, kv head) work groups to give every CU several; prefill: tiles
     // with long key ranges are cut so that no work group carries many times the average work.
-    int64_t dec_keys = 0, tile_work = 0, n_tiles = 0;
+    int64_t dec_keys = 0, tile_work = 0;
     for (int32_t r = 0; r < N; ++r) {
         const int32_t q = qsl[r + 1] - qsl[r];
         const int64_t ctx = int64_t(seq_lens[r]) - q;
@@ -324,7 +324,6 @@ extern "C" cb_status cb_plan_attention(const int32_t *qsl, const int32_t *seq_le
             for (int32_t i0 = 0; i0 < q; i0 += tile_tokens) {
                 const int64_t hi = ctx + std::min(q, i0 + tile_tokens);
                 tile_work += hi - lo_of(ctx + i0);
-                ++n_tiles;
             }
         }
     }

@@ -273,3 +273,83 @@ def test_swap_out_and_back_preserves_outputs(torch_gpu):
         torch.cuda.synchronize()
         print(f"[gpu] swap round trip of row {r}: {n} pages", flush=True)
         assert torch.equal(L.out, before)
+
+
+def test_prefix_sharing_step(torch_gpu):
+    """Two requests share the pages of a common prompt prefix through the prefix cache: A has prefilled 100 prompt
+    tokens (6 full blocks registered); B's prompt starts with the same 96 tokens, so B reuses A's first 6 pages and
+    prefills only its remaining 40 tokens, from context 96, while A decodes. The step's outputs match the oracle, and
+    B's rows are bitwise those of a run where B holds private copies of the prefix pages."""
+    import torch
+    import paged_kv_attention_varlen_amd as cb
+    from oracle import prefix_cache as O
+    from synth import round_to_bf16
+    rng = np.random.default_rng(21)
+    P, Hq, Hkv, D, n_pages = 16, 8, 2, 128, 64
+    prompt_a = rng.integers(0, 30000, 100).astype(np.int32)
+    prompt_b = np.concatenate([prompt_a[:96], rng.integers(0, 30000, 40).astype(np.int32)])
+    pc = cb.PrefixCache(n_pages, np.arange(2, n_pages, dtype=np.int32))
+    pages_a = pc.allocate(-(-101 // P))                                # A's 100 keys plus this step's token
+    for b, h in enumerate(cb.block_hashes(prompt_a, P)):
+        pc.commit(int(pages_a[b]), h)
+    hb = cb.block_hashes(prompt_b[:-1], P)                              # blocks of B's prompt
+    shared = pc.match(hb)
+    assert shared.tolist() == pages_a[:6].tolist()
+    assert hb.tolist()[:6] == O.block_hashes(prompt_b[:-1], P)[:6]
+    ctx_b = shared.size * P                                             # B skips the prefill of 96 tokens
+    pages_b = np.concatenate([shared, pc.allocate(-(-len(prompt_b) // P) - shared.size)])
+    assert pc.page_info(int(shared[0]))[0] == 2                         # both requests hold the shared page
+
+    # caches: A's history (100 keys) on its pages; B's context is A's (same tokens, same pages)
+    kc = np.full((n_pages, P, Hkv, D), np.nan, np.float32)
+    vc = np.full((n_pages, P, Hkv, D), np.nan, np.float32)
+    hist_k = round_to_bf16(rng.standard_normal((100, Hkv, D)).astype(np.float32))
+    hist_v = round_to_bf16(rng.standard_normal((100, Hkv, D)).astype(np.float32))
+    for pos in range(100):
+        kc[pages_a[pos // P], pos % P] = hist_k[pos]
+        vc[pages_a[pos // P], pos % P] = hist_v[pos]
+    # the step: A decodes 1 token at position 100, B prefills 40 at positions 96..135
+    qsl = np.array([0, 1, 41], np.int32)
+    seq = np.array([101, ctx_b + 40], np.int32)
+    width = max(pages_a.size, pages_b.size)
+    table = np.zeros((2, width), np.int32)
+    table[0, :pages_a.size], table[1, :pages_b.size] = pages_a, pages_b
+    new_k = round_to_bf16(rng.standard_normal((41, Hkv, D)).astype(np.float32))
+    new_v = round_to_bf16(rng.standard_normal((41, Hkv, D)).astype(np.float32))
+    q = round_to_bf16(rng.standard_normal((41, Hq, D)).astype(np.float32))
+    pos_of = [100] + list(range(ctx_b, ctx_b + 40))
+    rows_of = [0] + [1] * 40
+    slots = np.array([table[r][p // P] * P + p % P for r, p in zip(rows_of, pos_of)], np.int32)
+
+    def run(tab, kcache, vcache):
+        kd = torch.from_numpy(kcache.transpose(0, 2, 1, 3).copy()).to(torch.bfloat16).cuda()
+        vd = torch.from_numpy(vcache.transpose(0, 2, 3, 1).copy()).to(torch.bfloat16).cuda()
+        sl = np.array([tab[r][p // P] * P + p % P for r, p in zip(rows_of, pos_of)], np.int32)
+        cb.kv_append(kd, vd, torch.from_numpy(new_k).to(torch.bfloat16).cuda(),
+                     torch.from_numpy(new_v).to(torch.bfloat16).cuda(), torch.from_numpy(sl).cuda())
+        qd = torch.from_numpy(q).to(torch.bfloat16).cuda()
+        out = torch.full_like(qd, float("nan"))
+        plan = cb.plan_attention(qsl, seq, None, Hq, Hkv, D, P, "bf16", -1, 0, 0)
+        pd = torch.from_numpy(plan.buffer).cuda()
+        ws = torch.empty(max(1, cb.workspace_size(plan)), dtype=torch.uint8, device="cuda")
+        cb.paged_attention(out, qd, kd, vd, torch.from_numpy(tab).cuda(), plan, pd, 1 / np.sqrt(D), ws)
+        torch.cuda.synchronize()
+        return out
+
+    got = run(table, kc, vc)
+    # oracle: the append, then attention through the shared block table
+    ko, vo = kc.copy(), vc.copy()
+    A.kv_append(ko, vo, new_k, new_v, slots, P)
+    ref = A.paged_attention(q, ko.astype(np.float64), vo.astype(np.float64), qsl, seq, table, P, 1 / np.sqrt(D))
+    err = np.abs(got.float().cpu().numpy() - ref)
+    assert err.max() <= H.TOL_BF16_MAX and err.mean() <= H.TOL_BF16_MEAN
+    # without sharing: B's prefix copied to private pages 40.. ; B's rows are bitwise the same
+    private = table.copy()
+    private[1, :6] = np.arange(40, 46)
+    kp, vp = kc.copy(), vc.copy()
+    kp[40:46], vp[40:46] = kc[pages_a[:6]], vc[pages_a[:6]]
+    alone = run(private, kp, vp)
+    assert torch.equal(got[1:], alone[1:])
+    pc.release(pages_a)
+    pc.release(pages_b)
+    assert pc.stats()[1] == 6                                            # A's registered blocks stay initialized
