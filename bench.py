@@ -73,14 +73,24 @@ def algorithmic_work(w, sched):
     return out
 
 
+def decode_source_sha() -> str:
+    """SHA-256 of the decode kernel's source: the shared device helpers at the top of the device source and the
+    split-KV decode section. Edits elsewhere (append, prefill, merge) leave the decode kernel, and its measured
+    traffic, unchanged."""
+    src = open(DEVICE_SRC, encoding="utf-8").read()
+    helpers = src[:src.index("// ============================================================================================== KV append")]
+    start = src.index("// ===================================================================== split-KV decode")
+    end = src.index("// ========================================================================= general per-token kernel")
+    return hashlib.sha256((helpers + src[start:end]).encode()).hexdigest()
+
+
 def stored_traffic():
-    """HBM bytes per decode launch from a rocprofv3 counter run, if taken on the current kernel source."""
+    """HBM bytes per decode launch from a rocprofv3 counter run, if taken on the current decode kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        sha = hashlib.sha256(open(DEVICE_SRC, "rb").read()).hexdigest()
-        if rec.get("source_sha256") != sha:
+        if rec.get("decode_source_sha256") != decode_source_sha():
             return None
         return rec.get("traffic_bytes_per_launch")
     except Exception:  # noqa: BLE001
