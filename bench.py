@@ -84,13 +84,14 @@ def decode_source_sha() -> str:
     return hashlib.sha256((helpers + src[start:end]).encode()).hexdigest()
 
 
-def stored_traffic():
-    """HBM bytes per decode launch from a rocprofv3 counter run, if taken on the current decode kernel source."""
+def stored_traffic(workload: int):
+    """HBM bytes per decode launch from a rocprofv3 counter run, if taken on this workload and on the current decode
+    kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        if rec.get("decode_source_sha256") != decode_source_sha():
+        if rec.get("decode_source_sha256") != decode_source_sha() or rec.get("workload") != workload:
             return None
         return rec.get("traffic_bytes_per_launch")
     except Exception:  # noqa: BLE001
@@ -292,7 +293,7 @@ def main():
         achieved = dec_b / (dec_t / 1e3) / 1e9
         roofline = {"bound": "hbm", "kernel": "decode_kernel (split-KV decode)", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": stored_traffic(), "algorithmic_bytes_per_step": dec_b,
+                    "traffic": stored_traffic(args.workload), "algorithmic_bytes_per_step": dec_b,
                     "launches_per_step": sum(1 for x in work if x["decodes"]),
                     "avg_launch_us": round(dec_t * 1e3 / max(1, sum(1 for x in work if x["decodes"])), 2),
                     "timed_steps_sampled": len(timed)}
@@ -301,7 +302,10 @@ def main():
     roofline_prefill = None
     if pre_f > 0 and pre_t > 0:
         tf = pre_f / (pre_t / 1e3) / 1e12
-        roofline_prefill = {"bound": "mfma", "kernel": "prefill_kernel (bf16 MFMA tiles)", "achieved": round(tf, 1),
+        # fp32 steps and shapes the MFMA tiles do not take run on the per-token VALU kernel instead
+        fast = all(L_.plan.counts()["prefill"] > 0 and L_.plan.counts()["rowwise"] == 0 for L_ in step.layers)
+        roofline_prefill = {"bound": "mfma", "kernel": "prefill_kernel (bf16 MFMA tiles)" if fast else
+                            "prefill_kernel and rowwise_kernel (per-token VALU)", "achieved": round(tf, 1),
                             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                             "algorithmic_flops_per_step": pre_f, "avg_launch_us": round(pre_t * 1e3 / L, 2),
                             "timed_steps_sampled": len(timed)}
