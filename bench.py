@@ -215,6 +215,7 @@ def main():
 
     import torch
     from paged_kv_attention_varlen_amd import load_library
+    from paged_kv_attention_varlen_amd.hip_events import HipEvent
     from paged_kv_attention_varlen_amd.step import Step, StepPipeline
     from synth import make_workload
 
@@ -260,14 +261,16 @@ def main():
     L = len(w.layers)
     # Every EVENTS_EVERY-th timed step brackets its decode, prefill and merge kernels with events (6 per layer); the
     # kernel averages come from that sample of the timed steps. Each event is a packet in the stream and costs the
-    # step a few microseconds, so the other steps run without them.
+    # step a little time, so the other steps run without them. The timing events are recorded without the
+    # system-scope fence (hipEventDisableSystemFence): they order nothing, and the cache write-back and invalidation
+    # of that fence would otherwise be charged to the kernel that follows the event.
     timed = list(range(0, args.steps, EVENTS_EVERY))
-    events = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)] for k in timed}
-    # torch creates the HIP event on its first record: do that here, outside the timed region
+    events = {k: [[HipEvent(timing=True, system_fence=False) for _ in range(6)] for _ in range(L)] for k in timed}
+    cur = torch.cuda.current_stream()
     for per_step in events.values():
         for per_layer in per_step:
             for ev in per_layer:
-                ev.record()
+                ev.record(cur)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):

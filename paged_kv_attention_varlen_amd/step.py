@@ -18,6 +18,7 @@ from typing import List, Optional
 
 import numpy as np
 
+from .hip_events import HipEvent
 from . import (CB_PHASE_COMBINE, CB_PHASE_DECODE, CB_PHASE_PREFILL, CB_PHASE_ROWWISE, AttnPlan, CbError, _abi,
                build_metadata, kv_append, paged_attention, plan_attention, workspace_size)
 
@@ -238,7 +239,9 @@ class StepPipeline:
         self.copier = torch.cuda.Stream(dev) if copy_stream else None
         # events are created once (torch creates the HIP event at its first record) and re-recorded every step
         self.copy_ev = [torch.cuda.Event(), torch.cuda.Event()]   # copy into buffer pair i finished
-        self.rel_ev = [torch.cuda.Event(), torch.cuda.Event()]    # last kernels reading device buffer i finished
+        # last kernels reading device buffer i finished: it only orders the next copy into that buffer after reads,
+        # so it is recorded without the system-scope fence
+        self.rel_ev = [HipEvent(system_fence=False), HipEvent(system_fence=False)]
         self.fork = torch.cuda.Event()
         self.join = torch.cuda.Event()
         for e in (*self.copy_ev, *self.rel_ev, self.fork, self.join):
@@ -295,7 +298,7 @@ class StepPipeline:
             # the copy waits only for the step that last read this device buffer, then runs beside the kernels of
             # the step in flight; the compute stream waits for it before this step's first kernel
             if self.released[i] is not None:
-                self.copier.wait_event(self.released[i])
+                self.released[i].wait(self.copier)
             with torch.cuda.stream(self.copier):
                 dev[:at].copy_(self.host[i][:at], non_blocking=True)
             ev.record(self.copier)
