@@ -227,9 +227,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ float sm_l[4][16];
     __shared__ int sm_page[kDecodeMaxPages];
 
-    const int32_t *it = items + int64_t(blockIdx.x) * 8;
+    // the kv head varies fastest in the linear block index, so work groups start in the plan's heaviest-first order
+    // across all heads (blocks are dispatched in index order)
+    const int item = int(blockIdx.x) / Hkv;
+    const int g = int(blockIdx.x) - item * Hkv;
+    const int32_t *it = items + int64_t(item) * 8;
     const int r = it[0], t = it[1], kv_lo = it[3], kv_hi = it[4], slot = it[5], ring = it[6];
-    const int g = blockIdx.y;
     const int G = Hq / Hkv;
     const int P = 1 << P_log2;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1020,7 +1023,7 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
                                       : a->phases;
 
     if (pl.n_decode > 0 && (ph & CB_PHASE_DECODE)) {
-        const dim3 grid(unsigned(pl.n_decode), unsigned(Hkv));
+        const dim3 grid{unsigned(pl.n_decode) * unsigned(Hkv), 1u, 1u};
         const uint16_t *qq = static_cast<const uint16_t *>(a->q);
         uint16_t *oo = static_cast<uint16_t *>(a->out);
         const uint16_t *kk = static_cast<const uint16_t *>(a->k_cache);
