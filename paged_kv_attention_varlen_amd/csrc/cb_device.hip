@@ -900,11 +900,14 @@ __global__ __launch_bounds__(256) void combine_kernel(T *__restrict__ out, const
     const int h = blockIdx.y * (256 / quads) + threadIdx.x / quads;
     const int d = 4 * (threadIdx.x % quads);
     if (h >= Hq) return;
+    // both loops are unrolled so that several splits' loads are in flight at once: the merge is latency-bound
     float M = kNegInf;
+#pragma unroll 4
     for (int s = 0; s < n; ++s) M = fmaxf(M, part_ml[((int64_t(first) + int64_t(s) * stride) * Hq + h) * 2]);
     float L = 0.f;
     f32x4 O = {0.f, 0.f, 0.f, 0.f};
     if (M != kNegInf) {
+#pragma unroll 4
         for (int s = 0; s < n; ++s) {
             const int64_t sl = int64_t(first) + int64_t(s) * stride;
             const float f = exp2f(part_ml[(sl * Hq + h) * 2] - M);
@@ -914,8 +917,14 @@ __global__ __launch_bounds__(256) void combine_kernel(T *__restrict__ out, const
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     T *o = out + (int64_t(t) * Hq + h) * D + d;
+    T res[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(O[e] * inv);
+    for (int e = 0; e < 4; ++e) res[e] = from_f32<T>(O[e] * inv);
+    if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint2 *>(o) = *reinterpret_cast<const uint2 *>(res);
+    } else {
+        *reinterpret_cast<u32x4 *>(o) = *reinterpret_cast<const u32x4 *>(res);
+    }
 }
 
 inline int ilog2(int x) {

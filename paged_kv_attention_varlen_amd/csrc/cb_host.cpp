@@ -329,7 +329,7 @@ extern "C" cb_status cb_plan_attention(const int32_t *qsl, const int32_t *seq_le
     }
     int32_t S = sh->decode_split;
     if (S == 0) {
-        const int64_t target_groups = 8 * kNumCUs;                       // work groups across all kv heads
+        const int64_t target_groups = 6 * kNumCUs;                       // work groups across all kv heads
         const int64_t per = ceil_div(dec_keys * Hkv, target_groups);
         S = int32_t(std::min<int64_t>(4096, std::max<int64_t>(256, ceil_div(per, 256) * 256)));
     }
