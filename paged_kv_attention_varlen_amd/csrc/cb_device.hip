@@ -102,61 +102,78 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // ============================================================================================== KV append
 //
-// One work group per (group of 8 consecutive tokens of the step, kv head). K rows are copied in 16-byte chunks.
-// V goes into d-major pages: when the 8 tokens fill 8 consecutive, 8-aligned offsets of one page -- the usual case
-// inside a prefill chunk -- each d-row receives one 16-byte run (two for fp32); otherwise each element is written
-// on its own. Tokens whose slot is negative or outside the pool are skipped.
+// One work group per (group of 16 consecutive tokens of the step, kv head). K rows are copied in 16-byte chunks.
+// V goes into d-major pages. The group is cut into runs of R = min(16, page size) tokens; a run whose tokens fill R
+// consecutive, R-aligned offsets of one page (the usual case inside a prefill chunk) gives every d-row of that page
+// R contiguous elements, written as 16-byte stores. With R = 16 both halves of a 32-byte d-row come from the same
+// work group, so whole 32-byte pieces of memory are written. Tokens outside such runs are written element by
+// element. Tokens whose slot is negative or outside the pool are skipped.
 
-constexpr int kAppendGroup = 8;
+constexpr int kAppendGroup = 16;
+constexpr int kAppendThreads = 256;
 
 template <typename T>
-__global__ __launch_bounds__(128) void kv_append_kernel(T *__restrict__ kc, T *__restrict__ vc,
-                                                        const T *__restrict__ kn, const T *__restrict__ vn,
-                                                        const int32_t *__restrict__ slots, int num_tokens,
-                                                        int num_pages, int P, int Hkv, int D) {
+__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(T *__restrict__ kc, T *__restrict__ vc,
+                                                                   const T *__restrict__ kn, const T *__restrict__ vn,
+                                                                   const int32_t *__restrict__ slots, int num_tokens,
+                                                                   int num_pages, int P, int Hkv, int D) {
     constexpr int E = 16 / sizeof(T);   // elements per 16 bytes
     constexpr int TG = kAppendGroup;
     __shared__ int64_t s_slot[TG];
+    __shared__ int s_run[TG];           // run r is a whole aligned run inside one page
     const int g = blockIdx.y;
     const int64_t t0 = int64_t(blockIdx.x) * TG;
     const int nt = int(min(int64_t(TG), int64_t(num_tokens) - t0));
     const int64_t pool = int64_t(num_pages) * P;
+    const int R = min(TG, P);
     if (threadIdx.x < TG) {
         int64_t sl = threadIdx.x < nt ? int64_t(slots[t0 + threadIdx.x]) : -1;
         s_slot[threadIdx.x] = (sl >= 0 && sl < pool) ? sl : -1;
     }
     __syncthreads();
-    const int cpr = D / E;   // 16-byte chunks per row
-    for (int c = threadIdx.x; c < nt * cpr; c += blockDim.x) {
-        const int i = c / cpr, cc = c % cpr;
-        const int64_t slot = s_slot[i];
-        if (slot < 0) continue;
-        const int64_t page = slot / P;
-        const int off = int(slot % P);
-        store16(kc + ((page * Hkv + g) * P + off) * D + int64_t(cc) * E,
-                load16(kn + ((t0 + i) * Hkv + g) * D + int64_t(cc) * E));
+    if (threadIdx.x < TG / R) {
+        const int i0 = threadIdx.x * R;
+        const int64_t s0 = s_slot[i0];
+        bool ok = R * int(sizeof(T)) >= 16 && i0 + R <= nt && s0 >= 0 && (s0 % P) % R == 0;
+        for (int i = 1; i < R; ++i) ok = ok && s_slot[i0 + i] == s0 + i;
+        s_run[threadIdx.x] = ok;
     }
-    const int64_t s0 = s_slot[0];
-    bool run = nt == TG && s0 >= 0 && (s0 % P) % TG == 0 && (s0 % P) + TG <= P;
-#pragma unroll
-    for (int i = 1; i < TG; ++i) run = run && s_slot[i] == s0 + i;
-    if (run) {
-        const int64_t page = s0 / P;
-        const int off = int(s0 % P);
-        for (int d = threadIdx.x; d < D; d += blockDim.x) {
-            T vals[TG];
-#pragma unroll
-            for (int i = 0; i < TG; ++i) vals[i] = vn[((t0 + i) * Hkv + g) * D + d];
-            T *dst = vc + ((page * Hkv + g) * D + d) * P + off;
-#pragma unroll
-            for (int q = 0; q < TG / E; ++q) store16(dst + q * E, *reinterpret_cast<const u32x4 *>(vals + q * E));
-        }
-    } else {
-        for (int c = threadIdx.x; c < nt * D; c += blockDim.x) {
-            const int i = c / D, d = c % D;
+    __syncthreads();
+    // Each pass issues all of a thread's loads (one K chunk; E tokens of one V d-row, a wave covering 64
+    // consecutive d) before its stores, so a work group waits for memory about once per pass.
+    const int cpr = D / E;             // 16-byte chunks per K row
+    const int nk = nt * cpr;           // K chunks
+    const int nv = (TG / E) * D;       // V chunks of E tokens
+    for (int base = 0; base < max(nk, nv); base += blockDim.x) {
+        const int c = base + int(threadIdx.x);
+        u32x4 kval = {0, 0, 0, 0};
+        int64_t kdst = -1;
+        if (c < nk) {
+            const int i = c / cpr, cc = c % cpr;
             const int64_t slot = s_slot[i];
-            if (slot < 0) continue;
-            vc[((slot / P * Hkv + g) * D + d) * P + slot % P] = vn[((t0 + i) * Hkv + g) * D + d];
+            if (slot >= 0) {
+                kval = load16(kn + ((t0 + i) * Hkv + g) * D + int64_t(cc) * E);
+                kdst = ((slot / P * Hkv + g) * P + slot % P) * D + int64_t(cc) * E;
+            }
+        }
+        const int qa = c / D, d = c % D;
+        const int i0 = qa * E;   // first token of the V chunk
+        const bool vact = c < nv && i0 < nt;
+        T vals[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            vals[e] = (vact && i0 + e < nt) ? vn[((t0 + i0 + e) * Hkv + g) * D + d] : T(0);
+        if (kdst >= 0) store16(kc + kdst, kval);
+        if (!vact) continue;
+        if (s_run[i0 / R]) {
+            const int64_t s0 = s_slot[i0];
+            store16(vc + ((s0 / P * Hkv + g) * D + d) * P + s0 % P, *reinterpret_cast<const u32x4 *>(vals));
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int64_t slot = i0 + e < nt ? s_slot[i0 + e] : -1;
+                if (slot >= 0) vc[((slot / P * Hkv + g) * D + d) * P + slot % P] = vals[e];
+            }
         }
     }
 }
@@ -961,12 +978,12 @@ extern "C" cb_status cb_kv_append(void *k_cache, void *v_cache, const void *k_ne
     const dim3 grid{static_cast<unsigned>(groups), static_cast<unsigned>(num_kv_heads), 1u};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == CB_DTYPE_F32) {
-        hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(128), 0, s,
+        hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(kAppendThreads), 0, s,
                            static_cast<float *>(k_cache), static_cast<float *>(v_cache),
                            static_cast<const float *>(k_new), static_cast<const float *>(v_new), d_slot_mapping,
                            num_tokens, num_pages, page_size, num_kv_heads, head_dim);
     } else {
-        hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(128), 0, s,
+        hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(kAppendThreads), 0, s,
                            static_cast<uint16_t *>(k_cache), static_cast<uint16_t *>(v_cache),
                            static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new),
                            d_slot_mapping, num_tokens, num_pages, page_size, num_kv_heads, head_dim);
