@@ -213,6 +213,51 @@ def test_pipeline_steps_match_oracle(torch_gpu, mode):
             assert len(pipe.graphs) == 2, "one graph per metadata buffer"
 
 
+def _append_slots(rng, P, n_pages, T):
+    """Slot patterns the append kernel treats differently: aligned whole-page runs, a run that starts mid-page and
+    crosses into the next page, a run broken by a skipped token, and scattered single slots; T is not a multiple of
+    the kernel's 16-token groups. Every slot is used at most once."""
+    c = int(rng.integers(0, n_pages - 1))                      # the crossing run uses pages c and c + 1
+    pages = [int(x) for x in rng.permutation(n_pages) if x not in (c, c + 1)]
+    slots = []
+    for k in range(2):                                         # whole pages, in order
+        slots += [pages[k] * P + o for o in range(P)][:32]
+    start = c * P + max(0, P - 5)
+    slots += [start + i for i in range(min(9, 2 * P - max(0, P - 5)))]
+    run = [pages[2] * P + o for o in range(min(P, 16))]        # a run with one token skipped
+    run[len(run) // 2] = -1
+    slots += run
+    free = [p_ * P + o for p_ in pages[3:] for o in range(P)]
+    rng.shuffle(free)
+    slots += free[:max(0, T - len(slots))]
+    return np.array(slots[:T], np.int32)
+
+
+@pytest.mark.parametrize("dtype,P", [("bf16", 16), ("bf16", 8), ("bf16", 32), ("bf16", 2), ("f32", 4), ("f32", 16)])
+def test_kv_append_slot_patterns(torch_gpu, dtype, P):
+    """cb_kv_append against the oracle's append, bit for bit, on hand-made slot patterns (whole-page runs, runs
+    crossing pages, skipped tokens, scattered slots); slots never written keep their NaN."""
+    import paged_kv_attention_varlen_amd as cb
+    torch = torch_gpu
+    rng = np.random.default_rng(11 + P)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    T = 93
+    n_pages, Hkv, D = max(40, 4 * T // P), 2, (128 if dtype == "bf16" else 64)
+    slots = _append_slots(rng, P, n_pages, T)
+    print(f"[gpu] append {dtype} P={P} T={T}", flush=True)
+    kc = torch.full((n_pages, Hkv, P, D), float("nan"), device="cuda").to(tdt)
+    vc = torch.full((n_pages, Hkv, D, P), float("nan"), device="cuda").to(tdt)
+    kn = torch.randn((T, Hkv, D), device="cuda").to(tdt)
+    vn = torch.randn((T, Hkv, D), device="cuda").to(tdt)
+    cb.kv_append(kc, vc, kn, vn, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    k_ref = np.full((n_pages, P, Hkv, D), np.nan, np.float32)
+    v_ref = np.full((n_pages, P, Hkv, D), np.nan, np.float32)
+    A.kv_append(k_ref, v_ref, kn.float().cpu().numpy(), vn.float().cpu().numpy(), slots, P)
+    assert H.same_bits(kc.float().cpu().numpy().transpose(0, 2, 1, 3), k_ref), "K cache differs"
+    assert H.same_bits(vc.float().cpu().numpy().transpose(0, 3, 1, 2), v_ref), "V cache differs"
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_copy_pages_bit_exact(torch_gpu, dtype):
     """cb_kv_copy_pages against the oracle's page copy: random page lists (some out of range, skipped), both
