@@ -47,6 +47,7 @@ def algorithmic_work(w, sched):
     """What the method must move or compute, per layer (no padding, no partial results).
 
     decode kernel bytes: every visible key of a decode row read once per kv head (K and V), plus its Q and O rows.
+    append bytes: every new token's K and V rows read once and written once into the caches.
     prefill flops: 4*D per (query row, head, visible key) -- QK^T and PV, causal count.
     kv bytes: every visible key of every request read once per kv head (K and V).
     """
@@ -69,16 +70,18 @@ def algorithmic_work(w, sched):
                 dec_bytes += int(n_vis[0]) * w.Hkv * 2 * w.D * e + 2 * w.Hq * w.D * e
             else:
                 pre_flops += int(n_vis.sum()) * 4 * w.D * w.Hq
-        out.append({"decode_bytes": dec_bytes, "prefill_flops": pre_flops, "kv_bytes": kv_bytes, "decodes": n_dec})
+        append_bytes = 4 * int(sched["num_tokens"]) * w.Hkv * w.D * e
+        out.append({"decode_bytes": dec_bytes, "prefill_flops": pre_flops, "kv_bytes": kv_bytes, "decodes": n_dec,
+                    "append_bytes": append_bytes})
     return out
 
 
 def decode_source_sha() -> str:
-    """SHA-256 of the decode kernel's source: the shared device helpers at the top of the device source and the
-    split-KV decode section. Edits elsewhere (append, prefill, merge) leave the decode kernel, and its measured
-    traffic, unchanged."""
+    """SHA-256 of the decode launch's source: the shared device helpers and the KV append at the top of the device
+    source (the append's work groups run inside the decode launch) and the split-KV decode section. Edits elsewhere
+    (page copies, prefill, merge) leave the decode launch, and its measured traffic, unchanged."""
     src = open(DEVICE_SRC, encoding="utf-8").read()
-    helpers = src[:src.index("// ============================================================================================== KV append")]
+    helpers = src[:src.index("// ============================================================================================ page copies")]
     start = src.index("// ===================================================================== split-KV decode")
     end = src.index("// ========================================================================= general per-token kernel")
     return hashlib.sha256((helpers + src[start:end]).encode()).hexdigest()
@@ -291,12 +294,17 @@ def main():
 
     dec_t = sum(float(np.mean(dec_ms[l])) for l in range(L) if work[l]["decodes"])
     dec_b = sum(x["decode_bytes"] for x in work)
+    # with the fused append, the decode launch also moves the step's new K/V rows into the caches
+    fused = pipe.fused and all(x["decodes"] for x in work)
+    app_b = sum(x["append_bytes"] for x in work) if fused else 0
     roofline = None
     if dec_t > 0:
-        achieved = dec_b / (dec_t / 1e3) / 1e9
-        roofline = {"bound": "hbm", "kernel": "decode_kernel (split-KV decode)", "achieved": round(achieved, 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": stored_traffic(args.workload), "algorithmic_bytes_per_step": dec_b,
+        achieved = (dec_b + app_b) / (dec_t / 1e3) / 1e9
+        label = "decode_kernel (split-KV decode, with the fused KV append)" if fused else \
+            "decode_kernel (split-KV decode)"
+        roofline = {"bound": "hbm", "kernel": label, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": stored_traffic(args.workload), "algorithmic_bytes_per_step": dec_b + app_b,
+                    "of_which_append_bytes": app_b,
                     "launches_per_step": sum(1 for x in work if x["decodes"]),
                     "avg_launch_us": round(dec_t * 1e3 / max(1, sum(1 for x in work if x["decodes"])), 2),
                     "timed_steps_sampled": len(timed)}

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 2
+#define CB_ABI_VERSION 3
 
 typedef int32_t cb_status;
 #define CB_OK 0
@@ -233,6 +233,17 @@ typedef struct cb_attn_args {
     size_t workspace_bytes;
     int32_t phases;               /* 0 = the whole step; else a mask of CB_PHASE_* launching only those kernels,
                                      in the fixed order (lets a caller bracket one kernel with events)           */
+    /* Optional fused append. With k_new set, the call also writes the step's new K/V rows into the caches, exactly
+     * as cb_kv_append would with the same arguments, and the caller does not call cb_kv_append for this step. The
+     * append runs in the call that launches the plan's first cache-reading phase (decode if the plan has decode
+     * items, else the per-token phase, else the prefill phase): inside the decode launch its work groups follow
+     * the decode work groups, and each decode row takes its own new key and value from k_new / v_new instead of
+     * the cache; otherwise it is a launch of its own ahead of the per-token and prefill kernels. All NULL / 0: the
+     * caches are only read. */
+    const void *k_new;            /* device [num_new][Hkv][D], the caches' element type                          */
+    const void *v_new;            /* device [num_new][Hkv][D]                                                    */
+    const int32_t *slot_mapping;  /* device [num_new]; negative or out-of-pool slots are skipped                 */
+    int32_t num_new;              /* must equal the plan's token count when k_new is set                         */
 } cb_attn_args;
 
 #define CB_PHASE_DECODE 1         /* split-KV decode kernel                                                     */
@@ -247,7 +258,8 @@ size_t cb_paged_attention_workspace_size(const cb_attn_args *args);
  * Attention of every token of the plan ("Continuous Batching" blog, sections "优化：偏移实现 Mask" and "扩展：vLLM
  * v1 中的实现": per request, keys 0..context_len+local_q through block_table; no mask is materialised).
  * Launches, in order on `stream`: the split-KV decode kernel, the general per-token kernel, the prefill-tile kernel,
- * then the merge of split rows. Reads the caches only. Page ids read from block_table are clamped into
+ * then the merge of split rows. Reads the caches only, unless the fused append is requested (k_new above). Page ids
+ * read from block_table are clamped into
  * [0, num_pages) so a corrupt table cannot fault the device (results are then meaningless).
  * Returns CB_OK, CB_E_INVAL, CB_E_UNSUPPORTED, CB_E_WORKSPACE or CB_E_HIP.
  */

@@ -362,10 +362,12 @@ def workspace_size(plan: AttnPlan) -> int:
 
 
 def paged_attention(out, q, k_cache, v_cache, block_table, plan: AttnPlan, plan_dev, scale: float,
-                    workspace=None, stream=None, phases: int = 0) -> None:
+                    workspace=None, stream=None, phases: int = 0, k_new=None, v_new=None, slot_mapping=None) -> None:
     """cb_paged_attention: out/q [T, Hq, D]; caches as in kv_append; block_table [N, width] int32; plan_dev = the
     plan's int32 buffer on the device; workspace: a device byte tensor of at least workspace_size(plan) bytes;
-    phases: 0 for the whole step, or a mask of CB_PHASE_* to launch only some of its kernels."""
+    phases: 0 for the whole step, or a mask of CB_PHASE_* to launch only some of its kernels.
+    k_new, v_new [T, Hkv, D] and slot_mapping [T] int32 (all or none): the fused append, which writes the step's new
+    K/V into the caches in the same launches (the caller then skips kv_append for the step)."""
     lib = _abi.load()
     for t, nm in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                   (block_table, "block_table"), (plan_dev, "plan")):
@@ -380,6 +382,19 @@ def paged_attention(out, q, k_cache, v_cache, block_table, plan: AttnPlan, plan_
     if plan_dev.numel() < plan.buffer.size or str(plan_dev.dtype) != "torch.int32":
         raise ValueError("plan_dev must hold the plan's int32 buffer")
     a = _args(out, q, k_cache, v_cache, block_table, plan, plan_dev, scale, workspace, phases)
+    if k_new is not None:
+        for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (slot_mapping, "slot_mapping")):
+            _check_dev(t, nm)
+        if tuple(k_new.shape) != (plan.info.num_tokens, sh.num_kv_heads, sh.head_dim) or v_new.shape != k_new.shape:
+            raise ValueError("k_new / v_new shape does not match the plan")
+        if slot_mapping.numel() != k_new.shape[0] or str(slot_mapping.dtype) != "torch.int32":
+            raise ValueError("slot_mapping must be int32 [T]")
+        if not (k_new.dtype == v_new.dtype == k_cache.dtype):
+            raise ValueError("dtype mismatch")
+        a.k_new, a.v_new, a.slot_mapping = k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr()
+        a.num_new = k_new.shape[0]
+    elif v_new is not None or slot_mapping is not None:
+        raise ValueError("k_new, v_new and slot_mapping go together")
     st = lib.cb_paged_attention(C.byref(a), _stream(stream))
     if st != CB_OK:
         raise CbError(st, "cb_paged_attention")

@@ -113,16 +113,14 @@ constexpr int kAppendGroup = 16;
 constexpr int kAppendThreads = 256;
 
 template <typename T>
-__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(T *__restrict__ kc, T *__restrict__ vc,
-                                                                   const T *__restrict__ kn, const T *__restrict__ vn,
-                                                                   const int32_t *__restrict__ slots, int num_tokens,
-                                                                   int num_pages, int P, int Hkv, int D) {
+__device__ __forceinline__ void append_group(T *__restrict__ kc, T *__restrict__ vc, const T *__restrict__ kn,
+                                             const T *__restrict__ vn, const int32_t *__restrict__ slots,
+                                             int num_tokens, int num_pages, int P, int Hkv, int D, int group, int g) {
     constexpr int E = 16 / sizeof(T);   // elements per 16 bytes
     constexpr int TG = kAppendGroup;
     __shared__ int64_t s_slot[TG];
     __shared__ int s_run[TG];           // run r is a whole aligned run inside one page
-    const int g = blockIdx.y;
-    const int64_t t0 = int64_t(blockIdx.x) * TG;
+    const int64_t t0 = int64_t(group) * TG;
     const int nt = int(min(int64_t(TG), int64_t(num_tokens) - t0));
     const int64_t pool = int64_t(num_pages) * P;
     const int R = min(TG, P);
@@ -176,6 +174,14 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(T *__restrict
             }
         }
     }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(T *__restrict__ kc, T *__restrict__ vc,
+                                                                   const T *__restrict__ kn, const T *__restrict__ vn,
+                                                                   const int32_t *__restrict__ slots, int num_tokens,
+                                                                   int num_pages, int P, int Hkv, int D) {
+    append_group(kc, vc, kn, vn, slots, num_tokens, num_pages, P, Hkv, D, int(blockIdx.x), int(blockIdx.y));
 }
 
 // ============================================================================================ page copies
@@ -236,20 +242,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                      const int32_t *__restrict__ block_table, int table_width,
                                                      int num_pages, const int32_t *__restrict__ items,
                                                      float *__restrict__ part_o, float *__restrict__ part_ml, int Hq,
-                                                     int Hkv, int P_log2, float scale_log2e) {
+                                                     int Hkv, int P_log2, float scale_log2e, int n_decode_groups,
+                                                     uint16_t *kc_w, uint16_t *vc_w, const uint16_t *kn,
+                                                     const uint16_t *vn, const int32_t *slots, int num_new) {
     constexpr int KB = D / 32;   // QK MFMAs per 16-key half tile
     constexpr int DB = D / 16;   // PV MFMAs (16 d-rows each)
     __shared__ float sm_o[4][D][17];
     __shared__ float sm_m[4][16];
     __shared__ float sm_l[4][16];
     __shared__ int sm_page[kDecodeMaxPages];
+    __shared__ __attribute__((aligned(16))) uint16_t sm_new[2][D];   // the row's own new K and V (fused append)
+
+    // Fused append (kn != null): the work groups after the decode work groups write the step's new K/V into the
+    // caches, running in the decode tail. Decode rows then must not read their own new key from the cache, where it
+    // may not have landed yet: the work group whose split ends at the row's position takes it from kn / vn.
+    if (int(blockIdx.x) >= n_decode_groups) {
+        const int L = int(blockIdx.x) - n_decode_groups;
+        append_group(kc_w, vc_w, kn, vn, slots, num_new, num_pages, 1 << P_log2, Hkv, D, L / Hkv, L % Hkv);
+        return;
+    }
 
     // the kv head varies fastest in the linear block index, so work groups start in the plan's heaviest-first order
     // across all heads (blocks are dispatched in index order)
     const int item = int(blockIdx.x) / Hkv;
     const int g = int(blockIdx.x) - item * Hkv;
     const int32_t *it = items + int64_t(item) * 8;
-    const int r = it[0], t = it[1], kv_lo = it[3], kv_hi = it[4], slot = it[5], ring = it[6];
+    const int r = it[0], t = it[1], pos = it[2], kv_lo = it[3], kv_hi = it[4], slot = it[5], ring = it[6];
+    const bool own_new = kn != nullptr && kv_hi == pos + 1;
     const int G = Hq / Hkv;
     const int P = 1 << P_log2;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -262,6 +281,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int32_t *bt = block_table + int64_t(r) * table_width;
         const int nblk = ((kv_hi - 1) >> P_log2) - blk0 + 1;
         for (int i = threadIdx.x; i < nblk; i += 256) sm_page[i] = lookup_page(bt, blk0 + i, ring, num_pages);
+    }
+
+    if (own_new && threadIdx.x < D / 4) {   // 16-byte pieces of the new K row, then of the new V row
+        const int half = int(threadIdx.x) / (D / 8), c = int(threadIdx.x) % (D / 8);
+        const uint16_t *src = (half ? vn : kn) + (int64_t(t) * Hkv + g) * D + 8 * c;
+        *reinterpret_cast<u32x4 *>(&sm_new[half][8 * c]) = load16(src);
     }
 
     // Q as the B operand of the QK product: head `col`, d = 32kb + 8rg .. +8
@@ -317,6 +342,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int base = tile << 5;
         const int key8 = base + 8 * rg;
         const bool edge = base < kv_lo || base + 32 > kv_hi;
+        if (own_new && tile == (pos >> 5)) {   // the row's own new key: K row and V column from the staged copy
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                if (base + krow0 + 4 * hf == pos)
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+                        b.k[hf][kb] = *reinterpret_cast<const u32x4 *>(&sm_new[0][32 * kb + 8 * rg]);
+            if (pos >= key8 && pos < key8 + 8) {
+                const int e = pos - key8;
+#pragma unroll
+                for (int bb = 0; bb < DB; ++bb) {
+                    const uint32_t v = sm_new[1][16 * bb + col];
+                    u32x4 x = b.v[bb];
+                    const uint32_t w = x[e >> 1];
+                    x[e >> 1] = (e & 1) ? ((w & 0x0000FFFFu) | (v << 16)) : ((w & 0xFFFF0000u) | v);
+                    b.v[bb] = x;
+                }
+            }
+        }
         if (edge) {
 #pragma unroll
             for (int bb = 0; bb < DB; ++bb) b.v[bb] = mask_keys8(b.v[bb], key8, kv_lo, kv_hi);
@@ -961,6 +1005,26 @@ bool shape_ok(const cb_attn_shape &s) {
 
 }  // namespace
 
+// Launch of the append kernel over all tokens (sizes already checked).
+static hipError_t launch_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new, const int32_t *slots,
+                         int32_t num_tokens, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t dtype, hipStream_t s) {
+    const int64_t groups = (int64_t(num_tokens) + kAppendGroup - 1) / kAppendGroup;
+    const dim3 grid{static_cast<unsigned>(groups), static_cast<unsigned>(num_kv_heads), 1u};
+    if (dtype == CB_DTYPE_F32) {
+        hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(kAppendThreads), 0, s,
+                           static_cast<float *>(k_cache), static_cast<float *>(v_cache),
+                           static_cast<const float *>(k_new), static_cast<const float *>(v_new), slots,
+                           num_tokens, num_pages, page_size, num_kv_heads, head_dim);
+    } else {
+        hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(kAppendThreads), 0, s,
+                           static_cast<uint16_t *>(k_cache), static_cast<uint16_t *>(v_cache),
+                           static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new), slots,
+                           num_tokens, num_pages, page_size, num_kv_heads, head_dim);
+    }
+    return hipGetLastError();
+}
+
 // ================================================================================================== C ABI
 
 extern "C" cb_status cb_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
@@ -975,20 +1039,10 @@ extern "C" cb_status cb_kv_append(void *k_cache, void *v_cache, const void *k_ne
     if (!k_cache || !v_cache || !k_new || !v_new || !d_slot_mapping) return CB_E_INVAL;
     const int64_t groups = (int64_t(num_tokens) + kAppendGroup - 1) / kAppendGroup;
     if (groups > INT32_MAX || num_kv_heads > 65535) return CB_E_UNSUPPORTED;
-    const dim3 grid{static_cast<unsigned>(groups), static_cast<unsigned>(num_kv_heads), 1u};
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dtype == CB_DTYPE_F32) {
-        hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(kAppendThreads), 0, s,
-                           static_cast<float *>(k_cache), static_cast<float *>(v_cache),
-                           static_cast<const float *>(k_new), static_cast<const float *>(v_new), d_slot_mapping,
-                           num_tokens, num_pages, page_size, num_kv_heads, head_dim);
-    } else {
-        hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(kAppendThreads), 0, s,
-                           static_cast<uint16_t *>(k_cache), static_cast<uint16_t *>(v_cache),
-                           static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new),
-                           d_slot_mapping, num_tokens, num_pages, page_size, num_kv_heads, head_dim);
-    }
-    return hipGetLastError() == hipSuccess ? CB_OK : CB_E_HIP;
+    return launch_append(k_cache, v_cache, k_new, v_new, d_slot_mapping, num_tokens, num_pages, page_size,
+                         num_kv_heads, head_dim, dtype, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? CB_OK
+               : CB_E_HIP;
 }
 
 extern "C" cb_status cb_kv_copy_pages(void *dst, const int32_t *d_dst_pages, int32_t dst_slots, const void *src,
@@ -1037,6 +1091,13 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
         return CB_E_INVAL;
     const size_t need = cb_paged_attention_workspace_size(a);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return CB_E_WORKSPACE;
+    // fused append: the call that runs the first cache-reading phase of the plan also appends the step's new K/V
+    const bool fuse = a->k_new != nullptr;
+    if (fuse && (!a->v_new || !a->slot_mapping || a->num_new != pl.num_tokens)) return CB_E_INVAL;
+    const int first_reader = pl.n_decode > 0    ? CB_PHASE_DECODE
+                             : pl.n_rowwise > 0 ? CB_PHASE_ROWWISE
+                             : pl.n_prefill > 0 ? CB_PHASE_PREFILL
+                                                : 0;
     float *part_o = static_cast<float *>(a->workspace);
     float *part_ml = need ? reinterpret_cast<float *>(static_cast<char *>(a->workspace) +
                                                       align256(size_t(pl.n_partials) * Hq * D * sizeof(float)))
@@ -1048,18 +1109,35 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
     const int32_t ph = a->phases == 0 ? (CB_PHASE_DECODE | CB_PHASE_ROWWISE | CB_PHASE_PREFILL | CB_PHASE_COMBINE)
                                       : a->phases;
 
+    const bool append_here = fuse && (ph & first_reader) != 0;
+    const int64_t append_groups = append_here ? (int64_t(a->num_new) + kAppendGroup - 1) / kAppendGroup * Hkv : 0;
+    if (int64_t(pl.n_decode) * Hkv + append_groups > INT32_MAX) return CB_E_UNSUPPORTED;
     if (pl.n_decode > 0 && (ph & CB_PHASE_DECODE)) {
-        const dim3 grid{unsigned(pl.n_decode) * unsigned(Hkv), 1u, 1u};
+        // with the fused append, its work groups follow the decode work groups in the same grid
+        const int n_dec = pl.n_decode * Hkv;
+        const dim3 grid{unsigned(n_dec + append_groups), 1u, 1u};
         const uint16_t *qq = static_cast<const uint16_t *>(a->q);
         uint16_t *oo = static_cast<uint16_t *>(a->out);
         const uint16_t *kk = static_cast<const uint16_t *>(a->k_cache);
         const uint16_t *vv = static_cast<const uint16_t *>(a->v_cache);
+        uint16_t *kw = append_here ? static_cast<uint16_t *>(const_cast<void *>(a->k_cache)) : nullptr;
+        uint16_t *vw = append_here ? static_cast<uint16_t *>(const_cast<void *>(a->v_cache)) : nullptr;
+        const uint16_t *kn = append_here ? static_cast<const uint16_t *>(a->k_new) : nullptr;
+        const uint16_t *vn = append_here ? static_cast<const uint16_t *>(a->v_new) : nullptr;
+        const int32_t *sm = append_here ? a->slot_mapping : nullptr;
         if (D == 128)
             hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,
-                               a->table_width, a->num_pages, plan + pl.off_decode, part_o, part_ml, Hq, Hkv, Pl, sl2e);
+                               a->table_width, a->num_pages, plan + pl.off_decode, part_o, part_ml, Hq, Hkv, Pl, sl2e,
+                               n_dec, kw, vw, kn, vn, sm, a->num_new);
         else
             hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,
-                               a->table_width, a->num_pages, plan + pl.off_decode, part_o, part_ml, Hq, Hkv, Pl, sl2e);
+                               a->table_width, a->num_pages, plan + pl.off_decode, part_o, part_ml, Hq, Hkv, Pl, sl2e,
+                               n_dec, kw, vw, kn, vn, sm, a->num_new);
+    } else if (append_here) {
+        // the plan's first cache reader is the per-token or the prefill kernel: append on its own launch first
+        if (launch_append(const_cast<void *>(a->k_cache), const_cast<void *>(a->v_cache), a->k_new, a->v_new,
+                          a->slot_mapping, a->num_new, a->num_pages, sh.page_size, Hkv, D, sh.dtype, s) != hipSuccess)
+            return CB_E_HIP;
     }
     if (pl.n_rowwise > 0 && (ph & CB_PHASE_ROWWISE)) {
         const dim3 grid(unsigned(pl.n_rowwise), unsigned(Hkv), unsigned((G + 15) / 16));

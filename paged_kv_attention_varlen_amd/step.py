@@ -61,15 +61,20 @@ class Step:
         L = self.layers[l]
         kv_append(L.k_cache, L.v_cache, L.k_new, L.v_new, L.slot_mapping)
 
-    def attend(self, l: int, phases: int = 0) -> None:
+    def attend(self, l: int, phases: int = 0, fused_append: bool = False) -> None:
+        """Attention of layer l; fused_append=True also appends the step's new K/V in the same launches."""
         L = self.layers[l]
+        extra = dict(k_new=L.k_new, v_new=L.v_new, slot_mapping=L.slot_mapping) if fused_append else {}
         paged_attention(L.out, L.q, L.k_cache, L.v_cache, L.block_table, L.plan, L.plan_dev, self.scale,
-                        L.workspace, phases=phases)
+                        L.workspace, phases=phases, **extra)
 
-    def run(self) -> None:
+    def run(self, fused_append: bool = False) -> None:
         for l in range(len(self.layers)):
-            self.append(l)
-            self.attend(l)
+            if fused_append:
+                self.attend(l, fused_append=True)
+            else:
+                self.append(l)
+                self.attend(l)
 
     PHASE_DECODE = CB_PHASE_DECODE
     PHASE_REST = CB_PHASE_ROWWISE | CB_PHASE_PREFILL | CB_PHASE_COMBINE
@@ -206,16 +211,20 @@ class StepPipeline:
     (decode streams HBM while prefill keeps the matrix cores busy) and joins both before the merge. copy_stream=True
     moves the metadata copy to a stream of its own, so that it overlaps the previous step's kernels instead of
     sitting between steps. graphs=True replays the step's kernels as a captured HIP graph whenever the step's launch
-    configuration (metadata buffer, plans, token count) was seen before. All streams have the default priority.
+    configuration (metadata buffer, plans, token count) was seen before. fused_append=True (the default, except with
+    concurrent=True, whose prefill kernels would race the append) has cb_paged_attention write the new K/V itself:
+    the append's work groups run after the decode work groups in the decode launch, in the decode kernel's tail,
+    instead of in a launch of their own. All streams have the default priority.
     """
 
     def __init__(self, w, step: Step, decode_split: int = 0, prefill_split: int = 0, concurrent: bool = False,
-                 copy_stream: bool = True, graphs: bool = False):
+                 copy_stream: bool = True, graphs: bool = False, fused_append: bool = True):
         from . import Scheduler
         torch = _torch()
         self.step = step
         self.w = w
         self.concurrent = concurrent
+        self.fused = fused_append and not concurrent
         pools = [{"ring_len": lay.ring_len, "window_left": lay.window_left,
                   "pool_pages": lay.num_pages - len(lay.padding_pages), "free_pages": lay.free_pages}
                  for lay in w.layers]
@@ -330,8 +339,14 @@ class StepPipeline:
             kc, vc, kn, vn, n_pages, rows = self.append_args[l]
             if T > rows:
                 raise ValueError("step has more new tokens than the pipeline's input rows")
-            self._check(lib.cb_kv_append(kc, vc, kn, vn, sm, T, n_pages, w.page_size, w.Hkv, w.D, self.dtype,
-                                         handle), "cb_kv_append")
+            a = self.args[l]
+            if self.fused:
+                a.k_new, a.v_new, a.slot_mapping, a.num_new = kn, vn, sm, T
+            else:
+                a.k_new = a.v_new = a.slot_mapping = None
+                a.num_new = 0
+                self._check(lib.cb_kv_append(kc, vc, kn, vn, sm, T, n_pages, w.page_size, w.Hkv, w.D, self.dtype,
+                                             handle), "cb_kv_append")
 
         def attend(l, phases, ev0=None, ev1=None, aux=False):
             bt, width, sm, info, plan = views[l]

@@ -78,6 +78,17 @@ def test_device_calls_reject_bad_arguments_without_launching():
     assert lib.cb_paged_attention(C.byref(a), None) == _abi.CB_E_INVAL     # null pointers
     a.phases = 99
     assert lib.cb_paged_attention(C.byref(a), None) == _abi.CB_E_INVAL
+    # fused append: k_new without v_new / slot_mapping, or a token count other than the plan's, is refused before
+    # any launch (the pointers below are never dereferenced)
+    a.phases = 0
+    a.out = a.q = a.k_cache = a.v_cache = a.block_table = a.plan = 4096
+    a.num_pages, a.table_width = 8, 4
+    a.plan_info.num_tokens = 3
+    a.k_new = 4096
+    assert lib.cb_paged_attention(C.byref(a), None) == _abi.CB_E_INVAL
+    a.v_new = a.slot_mapping = 4096
+    a.num_new = 2
+    assert lib.cb_paged_attention(C.byref(a), None) == _abi.CB_E_INVAL
     # page copies: sizes checked before any launch
     assert lib.cb_kv_copy_pages(None, None, 4, None, None, 4, 0, 4096, None) == _abi.CB_OK      # nothing to copy
     assert lib.cb_kv_copy_pages(None, None, 4, None, None, 4, -1, 4096, None) == _abi.CB_E_INVAL

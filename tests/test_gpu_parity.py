@@ -25,11 +25,13 @@ def torch_gpu():
     return torch
 
 
-def _run(w, **kw):
+def _run(w, fused=False, **kw):
+    """Build the step and run it: cb_kv_append then cb_paged_attention, or (fused) cb_paged_attention alone with the
+    new K/V passed in, appending them itself."""
     from paged_kv_attention_varlen_amd.step import Step
-    print(f"[gpu] {w.name} {kw}", flush=True)
+    print(f"[gpu] {w.name} fused={fused} {kw}", flush=True)
     st = Step.from_workload(w, **kw)
-    st.run()
+    st.run(fused_append=fused)
     import torch
     torch.cuda.synchronize()
     return st
@@ -42,10 +44,11 @@ def _check_pages(w, st, layer, pages=None):
     assert H.same_bits(v[ids], v_ref), "V cache differs"
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
-def test_reduced_workload_all_rows_and_pages(torch_gpu, idx):
+def test_reduced_workload_all_rows_and_pages(torch_gpu, idx, fused):
     w = make_workload(idx, mini=True)
-    st = _run(w)
+    st = _run(w, fused=fused)
     for l in range(len(w.layers)):
         mx, mean = H.compare(w, st, l, label=f"w{idx} reduced layer {l}")
         print(f"  layer {l}: max {mx:.3g} mean {mean:.3g}", flush=True)
@@ -71,7 +74,7 @@ def _sample_tokens(sched, rng, n_dec=12, per_chunk=6):
 @pytest.mark.parametrize("idx", [2, 3, 4, 5])
 def test_full_workload_sampled_rows(torch_gpu, idx):
     w = make_workload(idx)
-    st = _run(w)
+    st = _run(w, fused=True)       # the benchmark's launches: the append fused into cb_paged_attention
     rng = np.random.default_rng(100 + idx)
     sched = R.schedule(w)
     toks = _sample_tokens(sched, rng)
@@ -117,14 +120,15 @@ EDGE = {
 }
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("name", list(EDGE))
-def test_edge_cases(torch_gpu, name):
+def test_edge_cases(torch_gpu, name, fused):
     cfg = dict(EDGE[name])
     reqs = cfg.pop("reqs")
     ds = cfg.pop("decode_split", 0)
     ps = cfg.pop("prefill_split", 0)
     w = H.custom_workload(reqs, name=name, **cfg)
-    st = _run(w, decode_split=ds, prefill_split=ps)
+    st = _run(w, fused=fused, decode_split=ds, prefill_split=ps)
     print(f"  plan {st.layers[0].plan.counts()}", flush=True)
     H.compare(w, st, 0, label=name)
     _check_pages(w, st, 0)
@@ -189,26 +193,39 @@ def test_prefill_first_step(torch_gpu):
             _check_pages(w, st, l)
 
 
-@pytest.mark.parametrize("mode", ["copy stream", "copy on compute stream", "concurrent prefill", "graph replay"])
+PIPELINE_MODES = ["copy stream", "copy on compute stream", "concurrent prefill", "graph replay", "separate append",
+                  "per-phase launches with events"]
+
+
+@pytest.mark.parametrize("mode", PIPELINE_MODES)
 def test_pipeline_steps_match_oracle(torch_gpu, mode):
     """The benchmark's loop: steps prepared into alternating pinned/device buffers, launched with the lean path,
-    repeated; every repetition of the (unchanged) step must produce the oracle's rows."""
+    repeated; every repetition of the (unchanged) step must produce the oracle's rows, and the caches the oracle's
+    pages. The append is fused into cb_paged_attention except with concurrent prefill and in the separate-append
+    mode; the per-phase mode launches each kernel of the step on its own call, between timing events, as the
+    benchmark does for its sampled steps."""
     from paged_kv_attention_varlen_amd.step import Step, StepPipeline
     for idx in (3, 5):
         w = make_workload(idx, mini=True)
         st = Step.from_workload(w)
         pipe = StepPipeline(w, st, copy_stream=(mode != "copy on compute stream"),
-                            concurrent=(mode == "concurrent prefill"), graphs=(mode == "graph replay"))
-        print(f"[gpu] pipeline {mode} workload {idx}", flush=True)
+                            concurrent=(mode == "concurrent prefill"), graphs=(mode == "graph replay"),
+                            fused_append=(mode != "separate append"))
+        events = None
+        if mode == "per-phase launches with events":
+            events = [[torch_gpu.cuda.Event(enable_timing=True) for _ in range(6)] for _ in w.layers]
+        print(f"[gpu] pipeline {mode} workload {idx} fused={pipe.fused}", flush=True)
         # every repetition is checked; graph replays (from the third step on) alternate with eager work on the
         # same stream and host synchronisations
         for rep in range(5):
             for l in range(len(w.layers)):
                 st.layers[l].out.fill_(float("nan"))
-            pipe.run()
+            pipe.run(events)
             torch_gpu.cuda.synchronize()
             for l in range(len(w.layers)):
                 H.compare(w, st, l, label=f"pipeline {mode} w{idx} layer {l} repetition {rep}")
+        for l in range(len(w.layers)):
+            _check_pages(w, st, l)
         if mode == "graph replay":
             assert len(pipe.graphs) == 2, "one graph per metadata buffer"
 
