@@ -212,8 +212,9 @@ def test_pipeline_steps_match_oracle(torch_gpu, mode):
                             concurrent=(mode == "concurrent prefill"), graphs=(mode == "graph replay"),
                             fused_append=(mode != "separate append"))
         events = None
-        if mode == "per-phase launches with events":
-            events = [[torch_gpu.cuda.Event(enable_timing=True) for _ in range(6)] for _ in w.layers]
+        if mode == "per-phase launches with events":   # the benchmark's timing events (no system-scope fence)
+            from paged_kv_attention_varlen_amd.hip_events import HipEvent
+            events = [[HipEvent(timing=True, system_fence=False) for _ in range(6)] for _ in w.layers]
         print(f"[gpu] pipeline {mode} workload {idx} fused={pipe.fused}", flush=True)
         # every repetition is checked; graph replays (from the third step on) alternate with eager work on the
         # same stream and host synchronisations
@@ -228,6 +229,10 @@ def test_pipeline_steps_match_oracle(torch_gpu, mode):
             _check_pages(w, st, l)
         if mode == "graph replay":
             assert len(pipe.graphs) == 2, "one graph per metadata buffer"
+        if events is not None:   # the events bracketed the decode, prefill and merge launches of the last step
+            for l in range(len(w.layers)):
+                for a, b in ((0, 1), (2, 3), (4, 5)):
+                    assert events[l][a].elapsed_time(events[l][b]) >= 0.0
 
 
 def _append_slots(rng, P, n_pages, T):
