@@ -189,7 +189,8 @@ cb_status cb_plan_attention(const int32_t *query_start_loc, const int32_t *seq_l
  * page slot_mapping[t] / page_size at offset slot_mapping[t] % page_size, bit for bit. Tokens with a negative (or
  * out-of-pool) slot are skipped. slot_mapping is the scheduler's (Continuous Batching blog, section "扩展：vLLM v1
  * 中的实现": the scheduler builds slot_mapping with the rest of the metadata). Must be enqueued before
- * cb_paged_attention of the same step: the step's own keys are read back from the cache.
+ * cb_paged_attention of the same step: the step's own keys are read back from the cache. (cb_paged_attention can
+ * instead do the same append itself, in its own launches: see k_new in cb_attn_args.)
  * Device pointers: k_cache, v_cache (layouts above), k_new, v_new [T][Hkv][D], d_slot_mapping [T].
  * Two tokens with the same slot race (last writer wins, unspecified which).
  */
