@@ -62,6 +62,20 @@ class PrefixCache:
             pages.append(p)
         return pages
 
+    def lookup(self, hashes):
+        """Pages of the leading blocks of `hashes` that are registered, without taking references."""
+        pages = []
+        for h in hashes:
+            p = self.index.get(int(h))
+            if p is None:
+                break
+            pages.append(p)
+        return pages
+
+    def n_free(self) -> int:
+        """Pages a fresh allocation can take: empty ones plus initialized ones (which it would demote)."""
+        return len(self.empty) + len(self.initialized)
+
     def allocate(self, n: int):
         if len(self.empty) + len(self.initialized) < n:
             return None                          # no space: nothing taken

@@ -42,7 +42,7 @@ FIFO, PREFILL_FIRST = "fifo", "prefill_first"
 
 
 def build_metadata(requests, layers, max_batch_tokens, max_requests, page_size, safety_margin=0.0, pad_page=0,
-                   policy=FIFO):
+                   policy=FIFO, prefix_cache=None, prompt_hashes=None):
     """Schedule one step.
 
     requests: sequence with .state, .num_computed, .num_pending, .pages (list per layer), in arrival order.
@@ -53,6 +53,21 @@ def build_metadata(requests, layers, max_batch_tokens, max_requests, page_size, 
     is left of the budget; pages are taken from the free lists in that order. Either way the rows are laid out
     decodes first, then continuing prefills, then admitted requests, each group in scheduling order.
     Returns a dict (see module docstring); "status" is "ok", "inval" or "nospace".
+
+    prefix_cache (an oracle.prefix_cache.PrefixCache over the pool's pages) turns on prefix sharing at admission
+    (same page, sections "前缀缓存" and "准入"). Sharing is on only when every layer can share, i.e. every layer is a
+    full-attention layer (the page: sliding-window and hybrid models disable it); with a ring layer the cache is
+    ignored. Readings taken, with sharing on:
+      * one layer type (the cache manages one pool); every page the step takes comes from the cache's allocator
+        (its empty pages, then demoted initialized ones), not from the layer's free list;
+      * a waiting request whose prompt has not started (num_computed 0, no pages) first looks up the leading blocks of its
+        prompt, prompt_hashes[i] (chain hashes of its full prompt blocks); at most (num_pending - 1) // page_size
+        of them count, so that the step still computes at least one prompt token (the one whose output starts the
+        generation); their pages become its first pages and its context starts at matched * page_size;
+      * admission stays all-or-nothing: the match is taken only if the fresh pages for the rest of the chunk can be
+        allocated too, counting matched pages that sat free in the cache as leaving the free pool;
+      * the safety margin and every availability check use the cache's free pages.
+    The returned dict then also holds "matched_tokens" [N] (context reused from the cache per row).
     """
     if policy not in (FIFO, PREFILL_FIRST):
         return {"status": E_INVAL}
@@ -80,6 +95,8 @@ def build_metadata(requests, layers, max_batch_tokens, max_requests, page_size, 
 
     free = [np.asarray(lay["free_pages"], dtype=np.int32) for lay in layers]
     taken = [0] * L
+    sharing = prefix_cache is not None and L == 1 and all(lay["ring_len"] == 0 for lay in layers)
+    pc = prefix_cache if sharing else None
 
     def needs(rq, q):
         out = []
@@ -91,17 +108,23 @@ def build_metadata(requests, layers, max_batch_tokens, max_requests, page_size, 
                 out.append(max(0, _cdiv(rq.num_computed + q, P) - have))
         return out
 
+    def n_free(l):
+        return pc.n_free() if pc is not None else len(free[l]) - taken[l]
+
     def fits(nd):
-        return all(nd[l] <= len(free[l]) - taken[l] for l in range(L))
+        return all(nd[l] <= n_free(l) for l in range(L))
 
     def take(nd):
         got = []
         for l in range(L):
-            got.append(free[l][taken[l]:taken[l] + nd[l]].copy())
+            if pc is not None:
+                got.append(np.array(pc.allocate(nd[l]), dtype=np.int32))
+            else:
+                got.append(free[l][taken[l]:taken[l] + nd[l]].copy())
             taken[l] += nd[l]
         return got
 
-    rows = {DECODING: [], PREFILLING: [], WAITING: []}   # (request index, q_len, new pages per layer)
+    rows = {DECODING: [], PREFILLING: [], WAITING: []}   # (request index, q_len, new pages per layer, matched)
     stalled = []
     first_rejected = -1
     held = False
@@ -122,7 +145,7 @@ def build_metadata(requests, layers, max_batch_tokens, max_requests, page_size, 
             if not fits(nd):
                 stalled.append(i)
                 continue
-            rows[DECODING].append((i, 1, take(nd)))
+            rows[DECODING].append((i, 1, take(nd), 0))
             budget -= 1
 
     def prefills():
@@ -138,7 +161,7 @@ def build_metadata(requests, layers, max_batch_tokens, max_requests, page_size, 
             if not fits(nd):
                 stalled.append(i)
                 continue
-            rows[PREFILLING].append((i, q, take(nd)))
+            rows[PREFILLING].append((i, q, take(nd), 0))
             budget -= q
 
     def admit():
@@ -149,16 +172,33 @@ def build_metadata(requests, layers, max_batch_tokens, max_requests, page_size, 
                 continue
             if n_rows() >= max_requests or budget < 1:
                 break
-            if any(lay["pool_pages"] > 0 and (len(free[l]) - taken[l]) < safety_margin * lay["pool_pages"]
+            if any(lay["pool_pages"] > 0 and n_free(l) < safety_margin * lay["pool_pages"]
                    for l, lay in enumerate(layers)):
                 held = True
                 break
-            q = min(rq.num_pending, budget)
-            nd = needs(rq, q)
-            if not fits(nd):
+            hit = []
+            if pc is not None and rq.num_computed == 0 and len(rq.pages[0]) == 0 and prompt_hashes is not None:
+                cap = (rq.num_pending - 1) // P
+                hit = pc.lookup(list(prompt_hashes[i])[:cap])
+            m = len(hit) * P
+            q = min(rq.num_pending - m, budget)
+            if hit:
+                # the matched pages are the request's first pages; matched pages that sit free in the cache leave
+                # its free pool when matched
+                nd = [max(0, _cdiv(m + q, P) - len(hit))]
+                leaving = sum(1 for p_ in hit if pc.ref[p_] == 0)
+                ok = nd[0] <= n_free(0) - leaving
+            else:
+                nd = needs(rq, q)
+                ok = fits(nd)
+            if not ok:
                 first_rejected = i
                 break
-            rows[WAITING].append((i, q, take(nd)))
+            if hit:
+                got = np.array(pc.match(list(prompt_hashes[i])[:len(hit)]), dtype=np.int32)
+                rows[WAITING].append((i, q, [np.concatenate([got, take(nd)[0]])], m))
+            else:
+                rows[WAITING].append((i, q, take(nd), 0))
             budget -= q
 
     for stage in ((decodes, prefills, admit) if policy == FIFO else (prefills, admit, decodes)):
@@ -168,16 +208,17 @@ def build_metadata(requests, layers, max_batch_tokens, max_requests, page_size, 
     rows = rows[DECODING] + rows[PREFILLING] + rows[WAITING]
 
     N = len(rows)
-    q_lens = np.array([q for _, q, _ in rows], dtype=np.int64)
+    q_lens = np.array([q for _, q, _, _ in rows], dtype=np.int64)
     qsl = np.zeros(N + 1, dtype=np.int32)
     qsl[1:] = np.cumsum(q_lens)
     T = int(qsl[-1])
-    seq_lens = np.array([requests[i].num_computed + q for i, q, _ in rows], dtype=np.int32)
-    req_index = np.array([i for i, _, _ in rows], dtype=np.int32)
+    seq_lens = np.array([requests[i].num_computed + m + q for i, q, _, m in rows], dtype=np.int32)
+    req_index = np.array([i for i, _, _, _ in rows], dtype=np.int32)
 
     out = {"status": OK, "query_start_loc": qsl, "seq_lens": seq_lens, "req_index": req_index,
            "num_reqs": N, "num_tokens": T, "num_decodes": num_decodes, "stalled": np.array(stalled, np.int32),
-           "first_rejected": first_rejected, "held_by_margin": held, "layers": []}
+           "first_rejected": first_rejected, "held_by_margin": held, "layers": [],
+           "prefix_sharing": sharing, "matched_tokens": np.array([m for _, _, _, m in rows], dtype=np.int32)}
     if N == 0 and (stalled or first_rejected >= 0):
         out["status"] = E_NOSPACE
 
@@ -189,7 +230,7 @@ def build_metadata(requests, layers, max_batch_tokens, max_requests, page_size, 
             width = max((_cdiv(int(s), P) for s in seq_lens), default=0)
         table = np.full((N, width), pad_page, dtype=np.int32)
         slots = np.zeros(T, dtype=np.int32)
-        for r, (i, q, new) in enumerate(rows):
+        for r, (i, q, new, m) in enumerate(rows):
             rq = requests[i]
             pages = np.concatenate([np.asarray(rq.pages[l], dtype=np.int32), new[l]]).astype(np.int32)
             if R > 0:
@@ -198,7 +239,7 @@ def build_metadata(requests, layers, max_batch_tokens, max_requests, page_size, 
                 n = _cdiv(int(seq_lens[r]), P)
                 table[r, :n] = pages[:n]
             for j in range(q):
-                pos = rq.num_computed + j
+                pos = rq.num_computed + m + j
                 blk, off = pos // P, pos % P
                 phys = table[r, blk % R] if R > 0 else table[r, blk]
                 slots[qsl[r] + j] = phys * P + off
