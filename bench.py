@@ -1,20 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark of one mixed continuous-batching step of paged attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--configs 2,3,4]
 
 A step is the whole hot path over one synthetic batch: host scheduling and planning into pinned memory, one
 host-to-device metadata copy, the KV append, split-KV decode, prefill tiles and the merge of split rows, for every
 layer of the workload. Kernels run back to back on one compute stream; the host prepares step k+1 (into the other
-of two pinned/device buffer pairs, copied on a stream of its own) while the device runs step k. Per-kernel durations
-come from HIP events recorded on the compute stream around the decode, prefill and merge kernels of every
-EVENTS_EVERY-th timed step. --concurrent instead runs the prefill-tile kernels on a second stream
-beside the decode kernel (their event intervals then overlap). Inputs (caches with the history, the step's new
-Q/K/V rows) are resident in HBM before timing starts.
+of two pinned/device buffer pairs, copied on a stream of its own) while the device runs step k. Inputs (caches with
+the history, the step's new Q/K/V rows) are resident in HBM before timing starts.
 
-Prints ONE JSON line on stdout; progress goes to stderr. The headline workload is the mixed chunked-prefill step
-under max_batch_tokens 2048 (96 decodes, two continuing 512-token chunks and a 928-token new prompt; 32 query /
-8 kv heads, head_dim 128, bf16, page 16).
+The headline is the largest single-GPU workload: the hybrid full + sliding-window layer pair over one 8192-token
+mixed step (128 decodes with context up to 32768, three 2048-token continuing chunks and a 1920-token new prompt;
+32 query / 8 kv heads, head_dim 128, bf16, page 32, window 4096). Exactly W untimed warm-up steps, then K timed
+steps between two device synchronisations: `value` is query tokens per second over those K steps (wall clock).
+Per-kernel durations come from fence-free HIP events recorded on the compute stream around the decode, prefill and
+merge launches of every EVENTS_EVERY-th timed step. A second pass of steps, each bracketed by step-boundary events,
+gives the p10/p50/p90 step times; a third runs steps after a 1 GiB write (larger than the 256 MB last-level cache)
+and reports the kernels' rooflines without a warm cache. The mixed 2048-token step, the decode-only step and the
+large decode batch are measured the same way and reported under `per_config`.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -35,7 +40,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 EVENTS_EVERY = 4               # every EVENTS_EVERY-th timed step carries the per-kernel timing events
-WARMUP_SECONDS = 0.3           # minimum duration of the untimed warm-up
+FLUSH_BYTES = 1 << 30          # the write between flushed steps
 DEVICE_SRC = os.path.join(ROOT, "paged_kv_attention_varlen_amd", "csrc", "cb_device.hip")
 
 
@@ -88,17 +93,19 @@ def decode_source_sha() -> str:
 
 
 def stored_traffic(workload: int):
-    """HBM bytes per decode launch from a rocprofv3 counter run, if taken on this workload and on the current decode
-    kernel source."""
+    """HBM bytes per step of the decode launches (all layers) from rocprofv3 counter runs, if taken on this workload
+    and on the current decode kernel source; None otherwise."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     try:
-        rec = json.load(open(TRAFFIC_FILE))
-        if rec.get("decode_source_sha256") != decode_source_sha() or rec.get("workload") != workload:
-            return None
-        return rec.get("traffic_bytes_per_launch")
+        recs = json.load(open(TRAFFIC_FILE)).get("records", [])
+        sha = decode_source_sha()
+        for rec in recs:
+            if rec.get("workload") == workload and rec.get("decode_source_sha256") == sha:
+                return rec.get("traffic_bytes_per_step")
     except Exception:  # noqa: BLE001
         return None
+    return None
 
 
 def measure_swap(step, n_pages: int, reps: int = 5) -> dict:
@@ -144,53 +151,206 @@ def measure_swap(step, n_pages: int, reps: int = 5) -> dict:
 
 
 def cpu_baseline(w, sched, seconds: float):
-    """Time the oracle (as it stands) on a bounded sample of the step's query rows: all decode rows first, then
-    prefill rows in random order, until `seconds` of oracle time (repeating the step if it finishes sooner). Input
-    generation is not timed."""
+    """Time the oracle (as it stands) on a bounded sample of the step's query rows, every layer of the workload:
+    the first decode rows one by one, then runs of up to 64 consecutive rows of the prefill chunks (random chunk,
+    random start), each run in one call of the oracle's row attention per layer, as the oracle computes a request's
+    rows. Stops after `seconds` of oracle time (or three times that of wall time, input generation included). Input
+    generation is not timed. A token counts once all layers' rows of it are done."""
     from oracle import attention as A
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
-        threads = 1
+        blas = None
     qsl, seq, idx = sched["query_start_loc"], sched["seq_lens"], sched["req_index"]
     nd = sched["num_decodes"]
-    order = [(r, 0) for r in range(nd)]
-    pre = [(r, i) for r in range(nd, sched["num_reqs"]) for i in range(int(qsl[r + 1] - qsl[r]))]
     rng = np.random.default_rng(0)
-    order += [pre[j] for j in rng.permutation(len(pre))]
-    layer = 0
-    wl = w.layers[layer].window_left
-    done, spent = 0, 0.0
-    # the whole step may take less than `seconds`: then its rows are timed again, pass after pass
-    passes = max(1, int(seconds // 2) + 1)
-    for r, i in (x for _ in range(passes) for x in order):
-        if spent >= seconds:
+    units = [(r, 0, 1) for r in range(min(nd, 8))]
+    chunks = list(range(nd, sched["num_reqs"]))
+    for _ in range(512):
+        if not chunks:
+            break
+        r = int(rng.choice(chunks))
+        q = int(qsl[r + 1] - qsl[r])
+        a = int(rng.integers(0, max(1, q - 63)))
+        units.append((r, a, min(q, a + 64)))
+    rows, spent, t_wall = 0, 0.0, time.perf_counter()
+    n_dec = n_pre = 0
+    for r, a, b in units:
+        if spent >= seconds or time.perf_counter() - t_wall > 3 * seconds:
             break
         q_len = int(qsl[r + 1] - qsl[r])
         ctx = int(seq[r]) - q_len
-        pos = ctx + i
-        lo = A.visible_range(pos, wl)[0]
-        k = w.values("k", int(idx[r]), layer, lo, pos + 1)
-        v = w.values("v", int(idx[r]), layer, lo, pos + 1)
-        qr = w.values("q", int(idx[r]), layer, pos, pos + 1)
-        t0 = time.perf_counter()
-        A.attend_rows(qr, k, v, lo, [pos], w.scale, wl)
-        spent += time.perf_counter() - t0
-        done += 1
-    return {"value": done / spent if spent > 0 else None, "unit": "query tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{done} query rows of layer '{w.layers[layer].name}' ({done / len(order):.2f} passes over "
-                      f"the step's {len(order)} rows: {nd} decode rows first, then the prefill rows in random "
-                      f"order), fp64 numpy, {spent:.1f} s"}
+        positions = list(range(ctx + a, ctx + b))
+        for l, lay in enumerate(w.layers):
+            lo = A.visible_range(positions[0], lay.window_left)[0]
+            k = w.values("k", int(idx[r]), l, lo, positions[-1] + 1)
+            v = w.values("v", int(idx[r]), l, lo, positions[-1] + 1)
+            qr = w.values("q", int(idx[r]), l, positions[0], positions[-1] + 1)
+            t0 = time.perf_counter()
+            A.attend_rows(qr, k, v, lo, positions, w.scale, lay.window_left)
+            spent += time.perf_counter() - t0
+        rows += b - a
+        if r < nd:
+            n_dec += 1
+        else:
+            n_pre += b - a
+    return {"value": rows / spent if spent > 0 else None, "unit": "query tokens/s",
+            "cores": len(os.sched_getaffinity(0)), "blas_threads": blas, "kind": "oracle",
+            "sample": f"{rows} query tokens of the headline step ({n_dec} decode rows, then {n_pre} prefill rows in "
+                      f"runs of up to 64 consecutive rows of one chunk), every layer "
+                      f"({', '.join(x.name for x in w.layers)}); fp64 numpy oracle, {spent:.1f} s of oracle time"}
+
+
+def _pct(xs):
+    a = np.asarray(xs, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 2), "p50": round(float(np.percentile(a, 50)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "n": int(a.size)}
+
+
+def _rooflines(w, step, work, fused, dec_us, pre_us, n_sampled):
+    """Decode roofline (HBM) and prefill roofline (MFMA) from per-layer mean kernel durations in microseconds."""
+    L = len(w.layers)
+    dec_t = sum(dec_us[l] for l in range(L) if work[l]["decodes"])
+    dec_b = sum(x["decode_bytes"] for x in work)
+    app_b = sum(x["append_bytes"] for x in work) if fused else 0
+    n_dec_launch = sum(1 for x in work if x["decodes"])
+    roofline = None
+    if dec_t > 0:
+        achieved = (dec_b + app_b) / (dec_t / 1e6) / 1e9
+        roofline = {"bound": "hbm", "kernel": "decode_kernel (split-KV decode" +
+                    (", with the fused KV append)" if fused else ")"),
+                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "algorithmic_bytes_per_step": dec_b + app_b, "of_which_append_bytes": app_b,
+                    "launches_per_step": n_dec_launch, "avg_launch_us": round(dec_t / max(1, n_dec_launch), 2),
+                    "per_layer_us": [round(dec_us[l], 2) for l in range(L)], "timed_steps_sampled": n_sampled}
+    pre_t = sum(pre_us[l] for l in range(L))
+    pre_f = sum(x["prefill_flops"] for x in work)
+    roofline_prefill = None
+    if pre_f > 0 and pre_t > 0:
+        tf = pre_f / (pre_t / 1e6) / 1e12
+        fast = all(L_.plan.counts()["prefill"] > 0 and L_.plan.counts()["rowwise"] == 0 for L_ in step.layers)
+        roofline_prefill = {"bound": "mfma", "kernel": "prefill_kernel (bf16 MFMA tiles)" if fast else
+                            "prefill_kernel and rowwise_kernel (per-token VALU)", "achieved": round(tf, 1),
+                            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                            "algorithmic_flops_per_step": pre_f, "avg_launch_us": round(pre_t / L, 2),
+                            "per_layer_us": [round(pre_us[l], 2) for l in range(L)],
+                            "timed_steps_sampled": n_sampled}
+    return roofline, roofline_prefill
+
+
+def measure(index: int, steps: int, warmup: int, args, dist_steps: int, flush_steps: int = 0):
+    """Set up a workload and time it (see the module docstring). Returns (result dict, workload, step, schedule)."""
+    import torch
+    from harness import build_step, pipeline_for
+    from paged_kv_attention_varlen_amd.hip_events import HipEvent
+    from synth import make_workload
+
+    w = make_workload(index)
+    log(f"[bench] workload {index}: {w.name}")
+    t = time.time()
+    step = build_step(w, decode_split=args.decode_split, prefill_split=args.prefill_split, threads=16)
+    pipe = pipeline_for(w, step, decode_split=args.decode_split, prefill_split=args.prefill_split,
+                        concurrent=args.concurrent, copy_stream=not args.no_copy_stream, graphs=args.graphs)
+    sched = step.sched
+    log(f"[bench] setup {time.time() - t:.1f}s; N={sched['num_reqs']} T={sched['num_tokens']} "
+        f"decodes={sched['num_decodes']}; plans {[L.plan.counts() for L in step.layers]}")
+    for _ in range(warmup):
+        pipe.run()
+    torch.cuda.synchronize()
+    L = len(w.layers)
+    main = pipe.main
+    # Every EVENTS_EVERY-th timed step brackets its decode, prefill and merge kernels with events (6 per layer); the
+    # kernel averages come from that sample of the timed steps. The timing events are recorded without the
+    # system-scope fence (hipEventDisableSystemFence): they order nothing, and the cache write-back and invalidation
+    # of that fence would otherwise be charged to the kernel that follows the event.
+    timed = list(range(0, steps, EVENTS_EVERY))
+    events = {k: [[HipEvent(timing=True, system_fence=False) for _ in range(6)] for _ in range(L)] for k in timed}
+    for per_step in events.values():
+        for per_layer in per_step:
+            for ev in per_layer:
+                ev.record(main)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        pipe.run(events.get(k))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    log(f"[bench] workload {index}: {steps} steps {ms_per_step:.4f} ms/step")
+
+    def mean_us(a, b):
+        return [float(np.mean([events[k][l][a].elapsed_time(events[k][l][b]) for k in timed])) * 1e3
+                for l in range(L)]
+
+    dec_us, pre_us, com_us = mean_us(0, 1), mean_us(2, 3), mean_us(4, 5)
+    work = algorithmic_work(w, sched)
+    fused = pipe.fused and all(x["decodes"] for x in work)
+    roofline, roofline_prefill = _rooflines(w, step, work, fused, dec_us, pre_us, len(timed))
+    if roofline is not None:
+        roofline["traffic"] = stored_traffic(index)
+
+    # step-time distribution: boundary events only, one per step
+    bounds = [HipEvent(timing=True, system_fence=False) for _ in range(dist_steps + 1)]
+    for k in range(dist_steps):
+        bounds[k].record(main)
+        pipe.run()
+    bounds[-1].record(main)
+    torch.cuda.synchronize()
+    step_us = [bounds[k].elapsed_time(bounds[k + 1]) * 1e3 for k in range(dist_steps)]
+
+    T = sched["num_tokens"]
+    kv_bytes = sum(x["kv_bytes"] for x in work)
+    res = {"workload": w.name, "index": index, "value": round(T / (ms_per_step / 1e3), 1),
+           "unit": "query tokens/s", "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
+           "step_us": _pct(step_us), "kv_gb_per_s": round(kv_bytes / (ms_per_step / 1e3) / 1e9, 1),
+           "requests": sched["num_reqs"], "query_tokens": T, "decodes": sched["num_decodes"],
+           "layers": [x.name for x in w.layers],
+           "kv_tokens_visible": int(kv_bytes // (w.Hkv * 2 * w.D * (2 if w.dtype == "bf16" else 4))),
+           "kernel_us": {"decode": round(sum(dec_us), 2), "prefill_and_rowwise": round(sum(pre_us), 2),
+                         "combine": round(sum(com_us), 2)},
+           "roofline": roofline, "roofline_prefill": roofline_prefill}
+
+    if flush_steps:
+        # each step after a 1 GiB write, steps synchronised one by one: the kernels start with a cold cache
+        scrub = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        fev = [[HipEvent(timing=True, system_fence=False) for _ in range(6)] for _ in range(L)]
+        fd, fp = [], []
+        for k in range(flush_steps):
+            scrub.fill_(float(k))
+            torch.cuda.synchronize()
+            pipe.run(fev)
+            torch.cuda.synchronize()
+            fd.append([fev[l][0].elapsed_time(fev[l][1]) * 1e3 for l in range(L)])
+            fp.append([fev[l][2].elapsed_time(fev[l][3]) * 1e3 for l in range(L)])
+        del scrub
+        fr, frp = _rooflines(w, step, work, fused, list(np.median(np.asarray(fd), axis=0)),
+                             list(np.median(np.asarray(fp), axis=0)), flush_steps)
+        res["flushed"] = {"steps": flush_steps, "write_bytes_before_each_step": FLUSH_BYTES,
+                          "decode_frac": fr["frac"] if fr else None,
+                          "decode_us": fr["avg_launch_us"] if fr else None,
+                          "prefill_frac": frp["frac"] if frp else None,
+                          "prefill_us": frp["avg_launch_us"] if frp else None}
+    if args.graphs:
+        res["graphs"] = {"captured": pipe.captures, "replayed": pipe.replays}
+    return res, w, step, pipe
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5],
+                    help="headline workload (default 5, the hybrid layer pair over one 8192-token step)")
+    ap.add_argument("--configs", default="2,3,4",
+                    help="comma-separated workloads also measured and reported under per_config ('' for none)")
+    ap.add_argument("--config-steps", type=int, default=50, help="timed steps of each per_config workload")
+    ap.add_argument("--config-warmup", type=int, default=10, help="warm-up steps of each per_config workload")
+    ap.add_argument("--dist-steps", type=int, default=40, help="steps of the step-time distribution pass")
+    ap.add_argument("--flush-steps", type=int, default=10,
+                    help="steps of the headline run after a 1 GiB write each (0: skip)")
     ap.add_argument("--decode-split", type=int, default=0)
     ap.add_argument("--prefill-split", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -201,8 +361,8 @@ def main():
                     help="copy each step's metadata on the compute stream instead of a stream of its own (which lets "
                          "the copy overlap the previous step's kernels)")
     ap.add_argument("--graphs", action="store_true",
-                    help="replay each step's kernels as a captured HIP graph (steps that carry timing events run "
-                         "eagerly)")
+                    help="replay each step's kernels as a HIP graph captured for its padded shape (steps that carry "
+                         "timing events run the same padded launches eagerly)")
     ap.add_argument("--swap-pages", type=int, default=0,
                     help="also measure offloading N cache pages of the first layer to pinned host memory and back "
                          "(gather kernel, device-to-host copy, host-to-device copy, scatter kernel)")
@@ -218,9 +378,6 @@ def main():
 
     import torch
     from paged_kv_attention_varlen_amd import load_library
-    from paged_kv_attention_varlen_amd.hip_events import HipEvent
-    from paged_kv_attention_varlen_amd.step import Step, StepPipeline
-    from synth import make_workload
 
     load_library()
     if not torch.cuda.is_available():
@@ -242,84 +399,21 @@ def main():
         copy_ref = {"bytes_read_plus_written": 2 * n * 4, "us": round(ms * 1e3, 1),
                     "gb_per_s": round(2 * n * 4 / (ms / 1e3) / 1e9, 1)}
         del src, dst
-    w = make_workload(args.workload)
-    log(f"[bench] workload {args.workload}: {w.name}")
-    t = time.time()
-    step = Step.from_workload(w, decode_split=args.decode_split, prefill_split=args.prefill_split, threads=16)
-    pipe = StepPipeline(w, step, args.decode_split, args.prefill_split, concurrent=args.concurrent,
-                        copy_stream=not args.no_copy_stream, graphs=args.graphs)
+
+    head, w, step, pipe = measure(args.workload, args.steps, args.warmup, args, args.dist_steps, args.flush_steps)
     sched = step.sched
-    log(f"[bench] setup {time.time() - t:.1f}s; N={sched['num_reqs']} T={sched['num_tokens']} "
-        f"decodes={sched['num_decodes']}; plans {[L.plan.counts() for L in step.layers]}")
+    swap = measure_swap(step, args.swap_pages) if args.swap_pages else None
+    del pipe, step
+    torch.cuda.empty_cache()
 
-    # untimed warm-up: at least W steps, and at least WARMUP_SECONDS of them so that the clocks have ramped up
-    warm, t_warm = 0, time.perf_counter()
-    while warm < args.warmup or time.perf_counter() - t_warm < WARMUP_SECONDS:
-        pipe.run()
-        warm += 1
-        if warm % 16 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    log(f"[bench] {warm} warm-up steps")
-    L = len(w.layers)
-    # Every EVENTS_EVERY-th timed step brackets its decode, prefill and merge kernels with events (6 per layer); the
-    # kernel averages come from that sample of the timed steps. Each event is a packet in the stream and costs the
-    # step a little time, so the other steps run without them. The timing events are recorded without the
-    # system-scope fence (hipEventDisableSystemFence): they order nothing, and the cache write-back and invalidation
-    # of that fence would otherwise be charged to the kernel that follows the event.
-    timed = list(range(0, args.steps, EVENTS_EVERY))
-    events = {k: [[HipEvent(timing=True, system_fence=False) for _ in range(6)] for _ in range(L)] for k in timed}
-    cur = torch.cuda.current_stream()
-    for per_step in events.values():
-        for per_layer in per_step:
-            for ev in per_layer:
-                ev.record(cur)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        pipe.run(events.get(k))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step")
-
-    # per-kernel durations from the events (same stream as the launches)
-    dec_ms = [[events[k][l][0].elapsed_time(events[k][l][1]) for k in timed] for l in range(L)]
-    pre_ms = [[events[k][l][2].elapsed_time(events[k][l][3]) for k in timed] for l in range(L)]
-    com_ms = [[events[k][l][4].elapsed_time(events[k][l][5]) for k in timed] for l in range(L)]
-    work = algorithmic_work(w, sched)
-    T = sched["num_tokens"]
-    value = T / (ms_per_step / 1e3)
-    kv_bytes = sum(x["kv_bytes"] for x in work)
-
-    dec_t = sum(float(np.mean(dec_ms[l])) for l in range(L) if work[l]["decodes"])
-    dec_b = sum(x["decode_bytes"] for x in work)
-    # with the fused append, the decode launch also moves the step's new K/V rows into the caches
-    fused = pipe.fused and all(x["decodes"] for x in work)
-    app_b = sum(x["append_bytes"] for x in work) if fused else 0
-    roofline = None
-    if dec_t > 0:
-        achieved = (dec_b + app_b) / (dec_t / 1e3) / 1e9
-        label = "decode_kernel (split-KV decode, with the fused KV append)" if fused else \
-            "decode_kernel (split-KV decode)"
-        roofline = {"bound": "hbm", "kernel": label, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": stored_traffic(args.workload), "algorithmic_bytes_per_step": dec_b + app_b,
-                    "of_which_append_bytes": app_b,
-                    "launches_per_step": sum(1 for x in work if x["decodes"]),
-                    "avg_launch_us": round(dec_t * 1e3 / max(1, sum(1 for x in work if x["decodes"])), 2),
-                    "timed_steps_sampled": len(timed)}
-    pre_t = sum(float(np.mean(pre_ms[l])) for l in range(L))
-    pre_f = sum(x["prefill_flops"] for x in work)
-    roofline_prefill = None
-    if pre_f > 0 and pre_t > 0:
-        tf = pre_f / (pre_t / 1e3) / 1e12
-        # fp32 steps and shapes the MFMA tiles do not take run on the per-token VALU kernel instead
-        fast = all(L_.plan.counts()["prefill"] > 0 and L_.plan.counts()["rowwise"] == 0 for L_ in step.layers)
-        roofline_prefill = {"bound": "mfma", "kernel": "prefill_kernel (bf16 MFMA tiles)" if fast else
-                            "prefill_kernel and rowwise_kernel (per-token VALU)", "achieved": round(tf, 1),
-                            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                            "algorithmic_flops_per_step": pre_f, "avg_launch_us": round(pre_t * 1e3 / L, 2),
-                            "timed_steps_sampled": len(timed)}
+    per_config = {}
+    for c in [int(x) for x in args.configs.split(",") if x.strip()]:
+        if c == args.workload:
+            continue
+        r, _, st, pp = measure(c, args.config_steps, args.config_warmup, args, args.dist_steps)
+        per_config[str(c)] = r
+        del st, pp
+        torch.cuda.empty_cache()
 
     base = None
     if not args.no_cpu_baseline:
@@ -327,21 +421,22 @@ def main():
         base = cpu_baseline(w, sched, args.cpu_seconds)
 
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": warm, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": head["value"], "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1) Q/K/V, shuffled page pools)",
-        "config": {"workload": w.name, "requests": sched["num_reqs"], "query_tokens": T,
-                   "decodes": sched["num_decodes"], "layers": [x.name for x in w.layers],
-                   "kv_tokens_visible": int(kv_bytes // (w.Hkv * 2 * w.D * (2 if w.dtype == "bf16" else 4)))},
-        "kv_gb_per_s": round(kv_bytes / (ms_per_step / 1e3) / 1e9, 1),
-        "kernel_us": {"decode": round(dec_t * 1e3, 2), "prefill_and_rowwise": round(pre_t * 1e3, 2),
-                      "combine": round(sum(float(np.mean(com_ms[l])) for l in range(L)) * 1e3, 2)},
-        "roofline": roofline, "roofline_prefill": roofline_prefill, "cpu_baseline": base,
+        "config": {"workload": w.name, "index": args.workload, "requests": head["requests"],
+                   "query_tokens": head["query_tokens"], "decodes": head["decodes"], "layers": head["layers"],
+                   "kv_tokens_visible": head["kv_tokens_visible"]},
+        "step_us": head["step_us"], "kv_gb_per_s": head["kv_gb_per_s"], "kernel_us": head["kernel_us"],
+        "roofline": head["roofline"], "roofline_prefill": head["roofline_prefill"],
+        "flushed": head.get("flushed"), "per_config": per_config, "cpu_baseline": base,
     }
+    if "graphs" in head:
+        line["graphs"] = head["graphs"]
     if copy_ref:
         line["device_copy_reference"] = copy_ref
-    if args.swap_pages:
-        line["kv_swap"] = measure_swap(step, args.swap_pages)
+    if swap:
+        line["kv_swap"] = swap
     print(json.dumps(line), flush=True)
 
 

@@ -22,10 +22,13 @@
  *     sliding layers.
  *   - Paging: key position p of request r lives in physical page block_table[r][p / page_size] at offset
  *     p % page_size; in ring mode (sliding layers) in page block_table[r][(p / page_size) % ring_len[r]].
- *   - Cache layouts (one tensor per layer for K and one for V, element type = the dtype):
+ *   - Cache layout (one tensor per layer for K and one for V, element type = the dtype). NOTE: this is NOT the
+ *     plain [num_pages][page_size][num_kv_heads][head_dim] order; V is transposed inside each page:
  *        k_cache  [num_pages][num_kv_heads][page_size][head_dim]   (key rows, head_dim contiguous)
  *        v_cache  [num_pages][num_kv_heads][head_dim][page_size]   (value columns, page offsets contiguous)
- *     So one kv head's slice of one page is a single contiguous run of page_size*head_dim elements in each tensor.
+ *     Callers state it with the tag CB_LAYOUT_KD_VT on every cache call (see "cache layout" below); the plain
+ *     order has its own tag, CB_LAYOUT_PAGED_NHD, which the kernels refuse. One kv head's slice of one page is a
+ *     single contiguous run of page_size*head_dim elements in each tensor.
  *   - Q and O are [T][num_q_heads][head_dim]; new K/V rows are [T][num_kv_heads][head_dim]. Query head h reads kv
  *     head h / (num_q_heads / num_kv_heads).
  *   - dtype: CB_DTYPE_F32 (float) or CB_DTYPE_BF16 (bfloat16). Attention accumulates in fp32; bf16 outputs are
@@ -43,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 3
+#define CB_ABI_VERSION 4
 
 typedef int32_t cb_status;
 #define CB_OK 0
@@ -144,6 +147,34 @@ typedef struct cb_step {
 cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const cb_sched_params *params,
                             const cb_layer_pool *layers, int32_t *out, int64_t out_capacity, cb_step *step);
 
+/*
+ * Cache slots of key positions lo .. hi-1 of one request: out[i] = page * page_size + (p % page_size) for p = lo + i,
+ * where page = pages[p / page_size] (full layers, ring_len 0) or pages[(p / page_size) % ring_len] (ring mode). This
+ * is the rule slot_mapping follows ("Continuous Batching" blog, section "扩展：vLLM v1 中的实现": logical block
+ * kv_pos / BLOCK_SIZE, offset kv_pos % BLOCK_SIZE, physical block from block_table), exposed for callers that write
+ * keys the scheduler did not schedule (a request's history, a swapped-in prompt). Host only.
+ * pages: host [n_pages], the request's block-table row (or ring). out: host [hi - lo], caller-owned.
+ * Returns CB_E_INVAL if a position needs an entry beyond n_pages, or on bad sizes (nothing is written then).
+ */
+cb_status cb_slot_mapping(const int32_t *pages, int32_t n_pages, int32_t ring_len, int32_t page_size, int32_t lo,
+                          int32_t hi, int32_t *out);
+
+/*
+ * Debug check of one layer's step metadata before it goes to the device (the kernels trust it and only clamp page
+ * ids into the pool, so a corrupt table gives meaningless rows instead of a fault). Checks, on host arrays:
+ * query_start_loc [N+1] starts at 0, never decreases and ends at num_tokens; seq_lens[r] >= q_len[r]; every
+ * block-table entry a row reads (its logical blocks 0 .. ceil(seq_len/page_size)-1, or its whole ring) is a page in
+ * [n_reserved, num_pages), i.e. inside the pool and not one of the reserved padding pages 0 .. n_reserved-1; every
+ * slot_mapping entry (if given) is the slot of its token's position under the same table, or negative (skipped).
+ * ring_len [N] or NULL (full layer). On failure returns CB_E_INVAL and writes to *bad_what a code (1 query_start_loc,
+ * 2 seq_lens, 3 block table, 4 slot_mapping) and to *bad_index the offending row or token (either pointer may be
+ * NULL). Host only, O(metadata).
+ */
+cb_status cb_validate_metadata(const int32_t *query_start_loc, const int32_t *seq_lens, int32_t num_reqs,
+                               const int32_t *block_table, int32_t table_width, const int32_t *ring_len,
+                               const int32_t *slot_mapping, int32_t num_tokens, int32_t num_pages, int32_t page_size,
+                               int32_t n_reserved, int32_t *bad_what, int32_t *bad_index);
+
 /* ------------------------------------------------------------------------------------------- cb_plan_attention */
 
 typedef struct cb_attn_shape {
@@ -153,8 +184,12 @@ typedef struct cb_attn_shape {
     int32_t page_size;         /* P: a power of two, 1..256                                                    */
     int32_t dtype;             /* CB_DTYPE_F32 or CB_DTYPE_BF16                                                */
     int32_t window_left;       /* -1: full attention; >= 0: sliding window                                     */
-    int32_t decode_split;      /* keys per decode split (a multiple of 64), 0 = chosen by the planner          */
-    int32_t prefill_split;     /* keys per prefill-tile split (a multiple of 64), 0 = chosen by the planner    */
+    int32_t decode_split;      /* keys per decode split (a multiple of 64), 0 = chosen by the planner from the
+                                  whole step's decode keys. Splits are merged in a fixed order, so a fixed value
+                                  makes a request's output bits independent of the rest of its batch; with 0 they
+                                  may change with the batch (the values stay within rounding of each other)    */
+    int32_t prefill_split;     /* keys per prefill-tile split (a multiple of 64), 0 = chosen by the planner
+                                  (batch-dependent in the same way as decode_split)                            */
 } cb_attn_shape;
 
 /* Header of the packed int32 plan. Work items (8 int32 each) and merge items (4 int32 each) start at the given
@@ -182,6 +217,29 @@ cb_status cb_plan_attention(const int32_t *query_start_loc, const int32_t *seq_l
                             int32_t num_reqs, const cb_attn_shape *shape, int32_t *out, int64_t out_capacity,
                             cb_plan *plan);
 
+/* ------------------------------------------------------------------------------------------------ cache layout */
+
+/*
+ * Cache layout tags. Every call that reads or writes a cache takes one, and refuses (CB_E_UNSUPPORTED, before any
+ * launch) a tag it does not implement, so a caller cannot silently pair its tensors with the wrong byte order.
+ *
+ *   CB_LAYOUT_PAGED_NHD (0)  k_cache and v_cache both [num_pages][page_size][num_kv_heads][head_dim]: the pages'
+ *                            own order k_cache[physical_block][block_offset] ("Continuous Batching" blog, section
+ *                            "扩展：vLLM v1 中的实现"), heads and head_dim appended. NOT implemented by the device
+ *                            kernels: passing it returns CB_E_UNSUPPORTED. It is 0 so that an argument block left
+ *                            zeroed is refused rather than misread.
+ *   CB_LAYOUT_KD_VT (1)      the layout this library implements. Page-major like the pages' order, with the inner
+ *                            order chosen for the bf16 matrix cores of gfx950:
+ *                              k_cache [num_pages][num_kv_heads][page_size][head_dim]   key rows, head_dim contiguous
+ *                              v_cache [num_pages][num_kv_heads][head_dim][page_size]   value columns, offsets contiguous
+ *                            Both contractions (q.k over head_dim, p.v over key offsets) then read their reduction
+ *                            index contiguously, 8 elements per lane, which is what an MFMA operand holds; the
+ *                            transposition of V is paid once per new token in the append instead of in every
+ *                            attention tile. One kv head's slice of a page is one contiguous run in each tensor.
+ */
+#define CB_LAYOUT_PAGED_NHD 0
+#define CB_LAYOUT_KD_VT 1
+
 /* ------------------------------------------------------------------------------------------------ cb_kv_append */
 
 /*
@@ -192,11 +250,12 @@ cb_status cb_plan_attention(const int32_t *query_start_loc, const int32_t *seq_l
  * cb_paged_attention of the same step: the step's own keys are read back from the cache. (cb_paged_attention can
  * instead do the same append itself, in its own launches: see k_new in cb_attn_args.)
  * Device pointers: k_cache, v_cache (layouts above), k_new, v_new [T][Hkv][D], d_slot_mapping [T].
+ * layout: CB_LAYOUT_KD_VT (anything else: CB_E_UNSUPPORTED).
  * Two tokens with the same slot race (last writer wins, unspecified which).
  */
 cb_status cb_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
                        const int32_t *d_slot_mapping, int32_t num_tokens, int32_t num_pages, int32_t page_size,
-                       int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void *stream);
+                       int32_t num_kv_heads, int32_t head_dim, int32_t dtype, int32_t layout, void *stream);
 
 /* -------------------------------------------------------------------------------------------- cb_kv_copy_pages */
 
@@ -223,6 +282,7 @@ typedef struct cb_attn_args {
     const void *q;                /* device [T][Hq][D]                                                           */
     const void *k_cache;          /* device, layout above                                                        */
     const void *v_cache;          /* device, layout above                                                        */
+    int32_t layout;               /* cache layout tag: must be CB_LAYOUT_KD_VT (else CB_E_UNSUPPORTED)           */
     const int32_t *block_table;   /* device [N][table_width]: physical page per logical block (or ring slot)     */
     const int32_t *plan;          /* device copy of the int32 plan written by cb_plan_attention                 */
     cb_plan plan_info;            /* host copy of that plan's header                                             */
@@ -245,6 +305,16 @@ typedef struct cb_attn_args {
     const void *v_new;            /* device [num_new][Hkv][D]                                                    */
     const int32_t *slot_mapping;  /* device [num_new]; negative or out-of-pool slots are skipped                 */
     int32_t num_new;              /* must equal the plan's token count when k_new is set                         */
+    /* Optional device-resident item counts, for launches whose shape must not change from step to step (a HIP graph
+     * captured once and replayed for every step that pads to the same shape: Transformers "continuous batching
+     * architecture" page, section "CUDA 图"). NULL: plan_info's counts are the items. Else device int32[4] =
+     * {n_decode, n_prefill, n_rowwise, n_combine} of THIS step, each <= the matching plan_info count, which is then
+     * only a capacity: the grids cover the capacities, the plan's sections are laid out at those capacities (the
+     * off_* offsets), and work groups past this step's counts exit at once. plan_info.n_partials must likewise be
+     * a capacity that stays the same across such steps: it fixes where the workspace's second region starts.
+     * Everything else the launches read (plan items, block table, slot mapping) is read from device memory too,
+     * so one captured launch serves every step whose metadata is written to the same addresses. */
+    const int32_t *counts;
 } cb_attn_args;
 
 #define CB_PHASE_DECODE 1         /* split-KV decode kernel                                                     */

@@ -18,13 +18,13 @@ import numpy as np
 
 from . import _abi
 from ._abi import (CB_DECODING, CB_DTYPE_BF16, CB_DTYPE_F32, CB_E_CAPACITY, CB_E_NOSPACE, CB_OK,  # noqa: F401
-                   CB_PHASE_COMBINE, CB_PHASE_DECODE, CB_PHASE_PREFILL, CB_PHASE_ROWWISE, CB_POLICY_FIFO,
+                   CB_LAYOUT_KD_VT, CB_LAYOUT_PAGED_NHD, CB_PHASE_COMBINE, CB_PHASE_DECODE, CB_PHASE_PREFILL, CB_PHASE_ROWWISE, CB_POLICY_FIFO,
                    CB_POLICY_PREFILL_FIRST, CB_PREFILLING, CB_WAITING, CbError)
 
 POLICIES = {"fifo": CB_POLICY_FIFO, "prefill_first": CB_POLICY_PREFILL_FIRST}
 
 __all__ = ["build_metadata", "plan_attention", "kv_append", "paged_attention", "workspace_size", "AttnPlan",
-           "Scheduler", "plan_into", "load_library", "CbError"]
+           "Scheduler", "Request", "advance", "schedule_arrays", "plan_into", "slot_mapping", "validate_metadata", "check_dtypes", "load_library", "CbError"]
 
 
 def load_library():
@@ -86,15 +86,95 @@ def build_metadata(requests, layers, max_batch_tokens: int, max_requests: int, p
         cap = int(step.used)
     if st not in (CB_OK, CB_E_NOSPACE):
         return {"status": st}
+    o = schedule_arrays(buf, step, L)
+    o["status"] = st
+    return o
+
+
+def slot_mapping(pages, ring_len: int, page_size: int, lo: int, hi: int) -> np.ndarray:
+    """cb_slot_mapping: cache slots of key positions lo .. hi-1 of a request owning `pages` (its block-table row,
+    or its ring of ring_len pages)."""
+    p = _i32(pages)
+    out = np.zeros(max(hi - lo, 1), dtype=np.int32)
+    st = _abi.load().cb_slot_mapping(_ptr(p), p.size, int(ring_len), int(page_size), int(lo), int(hi), _ptr(out))
+    if st != CB_OK:
+        raise CbError(st, "cb_slot_mapping")
+    return out[:max(hi - lo, 0)]
+
+
+def validate_metadata(query_start_loc, seq_lens, block_table, ring_len, slot_mapping, num_pages: int,
+                      page_size: int, n_reserved: int):
+    """cb_validate_metadata on host arrays. Returns None when the metadata is consistent, else (what, index) with
+    what in {"query_start_loc", "seq_lens", "block_table", "slot_mapping", "arguments"}."""
+    qsl, seq = _i32(query_start_loc), _i32(seq_lens)
+    bt = _i32(block_table)
+    width = bt.shape[1] if bt.ndim == 2 else 0
+    rl = None if ring_len is None else _i32(ring_len)
+    sm = None if slot_mapping is None else _i32(slot_mapping)
+    what, idx = C.c_int32(), C.c_int32()
+    st = _abi.load().cb_validate_metadata(_ptr(qsl), _ptr(seq), seq.size, _ptr(bt), width,
+                                          None if rl is None else _ptr(rl), None if sm is None else _ptr(sm),
+                                          int(qsl[-1]) if qsl.size else 0, int(num_pages), int(page_size),
+                                          int(n_reserved), C.byref(what), C.byref(idx))
+    if st == CB_OK:
+        return None
+    names = {0: "arguments", 1: "query_start_loc", 2: "seq_lens", 3: "block_table", 4: "slot_mapping"}
+    return names.get(what.value, "arguments"), idx.value
+
+
+@dataclass
+class Request:
+    """One request as the scheduler sees it (the fields of cb_req): state CB_DECODING / CB_PREFILLING / CB_WAITING,
+    keys already computed, tokens to feed next, and per layer type the pages it owns (logical order, or its ring)."""
+    id: int
+    state: int
+    num_computed: int
+    num_pending: int
+    pages: list
+
+
+def advance(requests, schedule: dict, free_pages, ring_lens, page_size: int):
+    """Request lifecycle after a step has run (Transformers "continuous batching architecture" page, section
+    "请求生命周期": a waiting request is admitted and prefilled in chunks, then decodes one token per step).
+
+    schedule: the step's metadata as `build_metadata` returns it (query_start_loc, seq_lens, req_index and per layer
+    the block table and used_pages). Every scheduled request has now computed its q_len tokens: a request whose
+    prompt is done decodes next (one pending token: the one this step produced), otherwise it keeps prefilling; its
+    pages are its block-table row (ceil(seq_len / page_size) pages, or its whole ring). Pages the step took leave the
+    front of each free list. Requests the step did not schedule are unchanged. Returns (requests, free_pages) as new
+    lists (Request records in the input order)."""
+    qsl, seq, idx = schedule["query_start_loc"], schedule["seq_lens"], schedule["req_index"]
+    out = [Request(int(r.id), int(r.state), int(r.num_computed), int(r.num_pending),
+                   [np.asarray(p, dtype=np.int32) for p in r.pages]) for r in requests]
+    for row in range(len(idx)):
+        rq = out[int(idx[row])]
+        q = int(qsl[row + 1] - qsl[row])
+        rq.num_computed += q
+        rq.num_pending -= q
+        if rq.num_pending <= 0:
+            rq.state, rq.num_pending = CB_DECODING, 1
+        else:
+            rq.state = CB_PREFILLING
+        for l, lay in enumerate(schedule["layers"]):
+            n = int(ring_lens[l]) if ring_lens[l] > 0 else -(-int(seq[row]) // page_size)
+            rq.pages[l] = np.array(lay["block_table"][row, :n], dtype=np.int32)
+    free = [np.asarray(f, dtype=np.int32)[int(lay["used_pages"]):].copy()
+            for f, lay in zip(free_pages, schedule["layers"])]
+    return out, free
+
+
+def schedule_arrays(buf: np.ndarray, step, n_layers: int) -> dict:
+    """The metadata cb_build_metadata wrote into `buf` (header `step`, n_layers layer types) as a dict of numpy
+    copies, in the form `build_metadata` returns."""
     N, T = step.num_reqs, step.num_tokens
-    o = {"status": st, "num_reqs": N, "num_tokens": T, "num_decodes": step.num_decodes,
+    o = {"status": CB_OK, "num_reqs": N, "num_tokens": T, "num_decodes": step.num_decodes,
          "max_q_len": step.max_q_len, "max_seq_len": step.max_seq_len,
          "query_start_loc": buf[step.off_query_start_loc:step.off_query_start_loc + N + 1].copy(),
          "seq_lens": buf[step.off_seq_lens:step.off_seq_lens + N].copy(),
          "req_index": buf[step.off_req_index:step.off_req_index + N].copy(),
          "stalled": buf[step.off_stalled:step.off_stalled + step.n_stalled].copy(),
          "first_rejected": step.first_rejected, "held_by_margin": bool(step.held_by_margin), "layers": []}
-    for l in range(L):
+    for l in range(n_layers):
         w = step.table_width[l]
         bt = buf[step.off_block_table[l]:step.off_block_table[l] + N * w].reshape(N, w).copy()
         o["layers"].append({"block_table": bt,
@@ -111,27 +191,49 @@ class Scheduler:
     def __init__(self, requests, layers, max_batch_tokens: int, max_requests: int, page_size: int,
                  safety_margin: float = 0.0, pad_page: int = 0, policy: str = "fifo"):
         self._lib = _abi.load()
-        self._keep = []
-        n, L = len(requests), len(layers)
-        self.n, self.L = n, L
-        self.reqs = (_abi.cb_req * max(n, 1))()
+        self.L = len(layers)
+        self.page_size = int(page_size)
+        self.pad_page = int(pad_page)
+        self.max_batch_tokens = int(max_batch_tokens)
+        self.max_requests = int(max_requests)
+        self.windows = [int(lay["window_left"]) for lay in layers]
+        self.rings = [int(lay["ring_len"]) for lay in layers]
+        self.params = _abi.cb_sched_params(int(max_batch_tokens), int(max_requests), int(page_size), int(pad_page),
+                                           self.L, POLICIES[policy], float(safety_margin))
+        self.set_state(requests, [lay["free_pages"] for lay in layers], [int(lay["pool_pages"]) for lay in layers])
+
+    def set_state(self, requests, free_pages, pool_pages=None) -> None:
+        """Replace the request list (arrival order) and the free lists, e.g. after a step has been taken."""
+        L = self.L
+        keep = []
+        n = len(requests)
+        self.n = n
+        self.requests = list(requests)
+        self.free_pages = [np.asarray(f, dtype=np.int32) for f in free_pages]
+        reqs = (_abi.cb_req * max(n, 1))()
         for i, rq in enumerate(requests):
-            r = self.reqs[i]
+            r = reqs[i]
             r.id, r.state, r.num_computed, r.num_pending = int(rq.id), int(rq.state), int(rq.num_computed), \
                 int(rq.num_pending)
             for l in range(L):
                 p = _i32(rq.pages[l])
-                self._keep.append(p)
+                keep.append(p)
                 r.n_pages[l] = p.size
                 r.pages[l] = _ptr(p)
-        self.pools = (_abi.cb_layer_pool * max(L, 1))()
-        for l, lay in enumerate(layers):
-            f = _i32(lay["free_pages"])
-            self._keep.append(f)
-            self.pools[l] = _abi.cb_layer_pool(int(lay["ring_len"]), int(lay["window_left"]), int(lay["pool_pages"]),
-                                               f.size, _ptr(f))
-        self.params = _abi.cb_sched_params(int(max_batch_tokens), int(max_requests), int(page_size), int(pad_page),
-                                           L, POLICIES[policy], float(safety_margin))
+        if pool_pages is None:
+            pool_pages = [self.pools[l].pool_pages for l in range(L)]
+        pools = (_abi.cb_layer_pool * max(L, 1))()
+        for l in range(L):
+            f = _i32(free_pages[l])
+            keep.append(f)
+            pools[l] = _abi.cb_layer_pool(self.rings[l], self.windows[l], int(pool_pages[l]), f.size, _ptr(f))
+        self.reqs, self.pools, self._keep = reqs, pools, keep
+
+    def advance(self, schedule: dict) -> None:
+        """After the step `schedule` has run: move every request along its lifecycle (`advance`) and drop the pages
+        the step took from the free lists."""
+        reqs, free = advance(self.requests, schedule, self.free_pages, self.rings, self.page_size)
+        self.set_state(reqs, free)
 
     def build_into(self, out: np.ndarray) -> _abi.cb_step:
         """Schedule into `out` (a C-contiguous int32 array); returns the header. Raises on any status but OK."""
@@ -241,7 +343,7 @@ def kv_append(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None) -> None
         raise ValueError("dtype mismatch")
     st = lib.cb_kv_append(k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
                           slot_mapping.data_ptr(), k_new.shape[0], n_pages, P, Hkv, D, _dtype_code(k_cache.dtype),
-                          _stream(stream))
+                          CB_LAYOUT_KD_VT, _stream(stream))
     if st != CB_OK:
         raise CbError(st, "cb_kv_append")
 
@@ -341,6 +443,7 @@ def _args(out, q, k_cache, v_cache, block_table, plan: AttnPlan, plan_dev, scale
     a = _abi.cb_attn_args()
     a.out, a.q = out.data_ptr(), q.data_ptr()
     a.k_cache, a.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+    a.layout = CB_LAYOUT_KD_VT
     a.block_table = block_table.data_ptr()
     a.plan = plan_dev.data_ptr()
     a.plan_info = plan.info
@@ -352,6 +455,18 @@ def _args(out, q, k_cache, v_cache, block_table, plan: AttnPlan, plan_dev, scale
     a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     a.phases = int(phases)
     return a
+
+
+def check_dtypes(plan: AttnPlan, **tensors) -> None:
+    """Raise ValueError unless every given tensor has the element type the plan was made for. The C ABI sees only
+    pointers, so this is the one place a bf16 plan paired with fp32 tensors (or the reverse) is caught before a
+    kernel would index them with the wrong element size."""
+    want = plan.shape.dtype
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if _dtype_code(t.dtype) != want:
+            raise ValueError(f"{name} has dtype {t.dtype}, the plan's dtype code is {want}")
 
 
 def workspace_size(plan: AttnPlan) -> int:
@@ -381,6 +496,9 @@ def paged_attention(out, q, k_cache, v_cache, block_table, plan: AttnPlan, plan_
         raise ValueError("v_cache shape does not match the plan")
     if plan_dev.numel() < plan.buffer.size or str(plan_dev.dtype) != "torch.int32":
         raise ValueError("plan_dev must hold the plan's int32 buffer")
+    check_dtypes(plan, q=q, out=out, k_cache=k_cache, v_cache=v_cache)
+    if str(block_table.dtype) != "torch.int32":
+        raise ValueError("block_table must be int32")
     a = _args(out, q, k_cache, v_cache, block_table, plan, plan_dev, scale, workspace, phases)
     if k_new is not None:
         for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (slot_mapping, "slot_mapping")):
@@ -389,8 +507,7 @@ def paged_attention(out, q, k_cache, v_cache, block_table, plan: AttnPlan, plan_
             raise ValueError("k_new / v_new shape does not match the plan")
         if slot_mapping.numel() != k_new.shape[0] or str(slot_mapping.dtype) != "torch.int32":
             raise ValueError("slot_mapping must be int32 [T]")
-        if not (k_new.dtype == v_new.dtype == k_cache.dtype):
-            raise ValueError("dtype mismatch")
+        check_dtypes(plan, k_new=k_new, v_new=v_new)
         a.k_new, a.v_new, a.slot_mapping = k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr()
         a.num_new = k_new.shape[0]
     elif v_new is not None or slot_mapping is not None:

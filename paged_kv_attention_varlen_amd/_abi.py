@@ -13,7 +13,8 @@ CB_DECODING, CB_PREFILLING, CB_WAITING = 0, 1, 2
 CB_MAX_LAYERS = 2
 CB_PHASE_DECODE, CB_PHASE_ROWWISE, CB_PHASE_PREFILL, CB_PHASE_COMBINE = 1, 2, 4, 8
 CB_POLICY_FIFO, CB_POLICY_PREFILL_FIRST = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
+CB_LAYOUT_PAGED_NHD, CB_LAYOUT_KD_VT = 0, 1
 
 i32p = C.POINTER(C.c_int32)
 
@@ -61,14 +62,14 @@ class cb_plan(C.Structure):
 
 class cb_attn_args(C.Structure):
     _fields_ = [("out", C.c_void_p), ("q", C.c_void_p), ("k_cache", C.c_void_p), ("v_cache", C.c_void_p),
-                ("block_table", C.c_void_p), ("plan", C.c_void_p), ("plan_info", cb_plan),
+                ("layout", C.c_int32), ("block_table", C.c_void_p), ("plan", C.c_void_p), ("plan_info", cb_plan),
                 ("shape", cb_attn_shape), ("num_pages", C.c_int32), ("table_width", C.c_int32),
                 ("scale", C.c_float), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
                 ("phases", C.c_int32), ("k_new", C.c_void_p), ("v_new", C.c_void_p), ("slot_mapping", C.c_void_p),
-                ("num_new", C.c_int32)]
+                ("num_new", C.c_int32), ("counts", C.c_void_p)]
 
 
-EXPORTS = ("cb_build_metadata", "cb_plan_attention", "cb_kv_append", "cb_kv_copy_pages", "cb_paged_attention",
+EXPORTS = ("cb_build_metadata", "cb_slot_mapping", "cb_validate_metadata", "cb_plan_attention", "cb_kv_append", "cb_kv_copy_pages", "cb_paged_attention",
            "cb_paged_attention_workspace_size", "cb_fnv1a64", "cb_block_hashes", "cb_pcache_create",
            "cb_pcache_destroy", "cb_pcache_match", "cb_pcache_allocate", "cb_pcache_commit", "cb_pcache_release",
            "cb_pcache_stats", "cb_pcache_page_info", "cb_status_str", "cb_abi_version")
@@ -99,7 +100,12 @@ def load(path: str = LIB_PATH):
                                       C.POINTER(cb_plan)]
     lib.cb_kv_append.restype = C.c_int32
     lib.cb_kv_append.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
-                                 C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
+                                 C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
+    lib.cb_slot_mapping.restype = C.c_int32
+    lib.cb_slot_mapping.argtypes = [i32p, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, i32p]
+    lib.cb_validate_metadata.restype = C.c_int32
+    lib.cb_validate_metadata.argtypes = [i32p, i32p, C.c_int32, i32p, C.c_int32, i32p, i32p, C.c_int32, C.c_int32,
+                                         C.c_int32, C.c_int32, i32p, i32p]
     lib.cb_kv_copy_pages.restype = C.c_int32
     lib.cb_kv_copy_pages.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                      C.c_int64, C.c_void_p]

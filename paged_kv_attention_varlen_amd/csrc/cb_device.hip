@@ -244,7 +244,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                      float *__restrict__ part_o, float *__restrict__ part_ml, int Hq,
                                                      int Hkv, int P_log2, float scale_log2e, int n_decode_groups,
                                                      uint16_t *kc_w, uint16_t *vc_w, const uint16_t *kn,
-                                                     const uint16_t *vn, const int32_t *slots, int num_new) {
+                                                     const uint16_t *vn, const int32_t *slots, int num_new,
+                                                     const int32_t *__restrict__ counts) {
     constexpr int KB = D / 32;   // QK MFMAs per 16-key half tile
     constexpr int DB = D / 16;   // PV MFMAs (16 d-rows each)
     __shared__ float sm_o[4][D][17];
@@ -266,6 +267,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // across all heads (blocks are dispatched in index order)
     const int item = int(blockIdx.x) / Hkv;
     const int g = int(blockIdx.x) - item * Hkv;
+    if (counts && item >= counts[0]) return;   // a launch sized for a capacity: past the step's decode items
     const int32_t *it = items + int64_t(item) * 8;
     const int r = it[0], t = it[1], pos = it[2], kv_lo = it[3], kv_hi = it[4], slot = it[5], ring = it[6];
     const bool own_new = kn != nullptr && kv_hi == pos + 1;
@@ -493,8 +495,10 @@ __global__ __launch_bounds__(64) void rowwise_kernel(const T *__restrict__ q, T 
                                                      const int32_t *__restrict__ block_table, int table_width,
                                                      int num_pages, const int32_t *__restrict__ items,
                                                      float *__restrict__ part_o, float *__restrict__ part_ml, int Hq,
-                                                     int Hkv, int P_log2, float scale_log2e) {
+                                                     int Hkv, int P_log2, float scale_log2e,
+                                                     const int32_t *__restrict__ counts) {
     constexpr int HG = 16;        // query heads per wave
+    if (counts && int(blockIdx.x) >= counts[2]) return;
     constexpr int DPL = D / 64;   // d values per lane in the V sum
     __shared__ float sq[HG][D];
     __shared__ float sp[HG][64];
@@ -648,7 +652,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint16_t *__restrict__ q, uint16_t *__restrict__ out, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ block_table, int table_width, int num_pages,
     const int32_t *__restrict__ items, int n_items, float *__restrict__ part_o, float *__restrict__ part_ml, int Hq,
-    int Hkv, float scale_log2e, int window_left) {
+    int Hkv, float scale_log2e, int window_left, const int32_t *__restrict__ counts) {
     constexpr int P = 1 << PL;
     constexpr int KB = D / 16;          // k-steps of the QK product
     constexpr int DB = D / 32;          // 32-row d blocks of the output
@@ -665,6 +669,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     int item, g;
     if (!xcd_item(blockIdx.x, n_items, Hkv, item, g)) return;
+    if (counts && item >= counts[1]) return;   // a launch sized for a capacity: past the step's prefill items
     const int32_t *it = items + int64_t(item) * 8;
     const int r = it[0], t0 = it[1], pos0 = it[2], qc = it[3], kv_lo = it[4], kv_hi = it[5];
     const int slot_base = it[6], ring = it[7];
@@ -954,7 +959,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(T *__restrict__ out, const float *__restrict__ part_o,
                                                       const float *__restrict__ part_ml,
-                                                      const int32_t *__restrict__ items, int Hq, int D) {
+                                                      const int32_t *__restrict__ items, int Hq, int D,
+                                                      const int32_t *__restrict__ counts) {
+    if (counts && int(blockIdx.x) >= counts[3]) return;
     const int32_t *it = items + int64_t(blockIdx.x) * 4;
     const int t = it[0], first = it[1], n = it[2], stride = it[3];
     const int quads = D / 4;
@@ -1030,9 +1037,10 @@ static hipError_t launch_append(void *k_cache, void *v_cache, const void *k_new,
 extern "C" cb_status cb_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
                                   const int32_t *d_slot_mapping, int32_t num_tokens, int32_t num_pages,
                                   int32_t page_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
-                                  void *stream) {
+                                  int32_t layout, void *stream) {
     if (num_tokens < 0 || num_pages < 1 || page_size < 1 || num_kv_heads < 1 || head_dim < 1) return CB_E_INVAL;
     if (dtype != CB_DTYPE_F32 && dtype != CB_DTYPE_BF16) return CB_E_UNSUPPORTED;
+    if (layout != CB_LAYOUT_KD_VT) return CB_E_UNSUPPORTED;
     const int esz = dtype == CB_DTYPE_F32 ? 4 : 2;
     if ((head_dim * esz) % 16 != 0) return CB_E_UNSUPPORTED;
     if (num_tokens == 0) return CB_OK;
@@ -1074,7 +1082,7 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
     if (!a || a->phases < 0 || a->phases > 15) return CB_E_INVAL;
     const cb_attn_shape &sh = a->shape;
     const cb_plan &pl = a->plan_info;
-    if (!shape_ok(sh)) return CB_E_UNSUPPORTED;
+    if (!shape_ok(sh) || a->layout != CB_LAYOUT_KD_VT) return CB_E_UNSUPPORTED;
     if (pl.n_decode < 0 || pl.n_prefill < 0 || pl.n_rowwise < 0 || pl.n_combine < 0 || pl.n_partials < 0)
         return CB_E_INVAL;
     const int64_t n_work = int64_t(pl.n_decode) + pl.n_prefill + pl.n_rowwise + pl.n_combine;
@@ -1128,11 +1136,11 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
         if (D == 128)
             hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,
                                a->table_width, a->num_pages, plan + pl.off_decode, part_o, part_ml, Hq, Hkv, Pl, sl2e,
-                               n_dec, kw, vw, kn, vn, sm, a->num_new);
+                               n_dec, kw, vw, kn, vn, sm, a->num_new, a->counts);
         else
             hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,
                                a->table_width, a->num_pages, plan + pl.off_decode, part_o, part_ml, Hq, Hkv, Pl, sl2e,
-                               n_dec, kw, vw, kn, vn, sm, a->num_new);
+                               n_dec, kw, vw, kn, vn, sm, a->num_new, a->counts);
     } else if (append_here) {
         // the plan's first cache reader is the per-token or the prefill kernel: append on its own launch first
         if (launch_append(const_cast<void *>(a->k_cache), const_cast<void *>(a->v_cache), a->k_new, a->v_new,
@@ -1145,7 +1153,7 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
     hipLaunchKernelGGL((rowwise_kernel<T, DD>), grid, dim3(64), 0, s, static_cast<const T *>(a->q),              \
                        static_cast<T *>(a->out), static_cast<const T *>(a->k_cache),                           \
                        static_cast<const T *>(a->v_cache), a->block_table, a->table_width, a->num_pages,        \
-                       plan + pl.off_rowwise, part_o, part_ml, Hq, Hkv, Pl, sl2e)
+                       plan + pl.off_rowwise, part_o, part_ml, Hq, Hkv, Pl, sl2e, a->counts)
         if (bf16) {
             if (D == 128) CB_ROWWISE(uint16_t, 128); else CB_ROWWISE(uint16_t, 64);
         } else {
@@ -1162,7 +1170,7 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
 #define CB_PREFILL(DD, PLOG)                                                                                   \
     hipLaunchKernelGGL((prefill_kernel<DD, PLOG>), grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,      \
                        a->table_width, a->num_pages, plan + pl.off_prefill, pl.n_prefill, part_o, part_ml, Hq, \
-                       Hkv, sl2e, sh.window_left)
+                       Hkv, sl2e, sh.window_left, a->counts)
 #define CB_PREFILL_D(DD)                                                                                       \
     switch (Pl) {                                                                                              \
         case 3: CB_PREFILL(DD, 3); break;                                                                      \
@@ -1185,10 +1193,11 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
         const dim3 grid(unsigned(pl.n_combine), unsigned((Hq + heads_per_group - 1) / heads_per_group));
         if (bf16)
             hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s, static_cast<uint16_t *>(a->out),
-                               part_o, part_ml, plan + pl.off_combine, Hq, D);
+                               part_o, part_ml, plan + pl.off_combine, Hq, D, a->counts);
         else
             hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, static_cast<float *>(a->out), part_o,
-                               part_ml, plan + pl.off_combine, Hq, D);
+                               part_ml, plan + pl.off_combine, Hq, D, a->counts);
     }
     return hipGetLastError() == hipSuccess ? CB_OK : CB_E_HIP;
 }
+

@@ -23,6 +23,14 @@ int64_t min_ring_pages(int32_t window_left, int32_t max_chunk, int32_t P) {
     return (int64_t(window_left) + max_chunk + P - 2) / P + 1;
 }
 
+// Slot of key position pos of a request whose block-table row (or ring of ring_len pages) is `row`: the physical
+// page of logical block pos / P (ring slot (pos / P) mod ring_len), times P, plus the offset pos % P.
+inline int64_t slot_of(const int32_t *row, int64_t pos, int32_t P, int32_t ring_len) {
+    const int64_t logical = pos / P;
+    const int32_t page = row[ring_len > 0 ? logical % ring_len : logical];
+    return int64_t(page) * P + pos % P;
+}
+
 struct Scheduled {
     int32_t req;                        // index into the caller's request array
     int32_t q;                          // tokens of this step
@@ -254,16 +262,61 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
                 row[b] = page;
             }
             rlen[r] = R;
-            for (int32_t j = 0; j < s.q; ++j) {
-                const int64_t pos = int64_t(rq.num_computed) + j;
-                const int64_t logical = pos / P;
-                const int32_t page = R > 0 ? row[logical % R] : row[logical];
-                slots[qsl[r] + j] = int32_t(int64_t(page) * P + pos % P);
-            }
+            for (int32_t j = 0; j < s.q; ++j)
+                slots[qsl[r] + j] = int32_t(slot_of(row, int64_t(rq.num_computed) + j, P, R));
         }
     }
     const bool blocked = !stalled.empty() || first_rejected >= 0;
     return (N == 0 && blocked) ? CB_E_NOSPACE : CB_OK;
+}
+
+extern "C" cb_status cb_slot_mapping(const int32_t *pages, int32_t n_pages, int32_t ring_len, int32_t page_size,
+                                     int32_t lo, int32_t hi, int32_t *out) {
+    if (page_size < 1 || n_pages < 0 || ring_len < 0 || lo < 0 || hi < lo) return CB_E_INVAL;
+    if (hi == lo) return CB_OK;
+    if (!pages || !out) return CB_E_INVAL;
+    // the largest table index any position reads must exist
+    const int64_t need = ring_len > 0 ? std::min<int64_t>(ring_len, ceil_div(hi, page_size)) : ceil_div(hi, page_size);
+    if (need > n_pages || (ring_len > 0 && ring_len > n_pages)) return CB_E_INVAL;
+    for (int32_t p = lo; p < hi; ++p) out[p - lo] = int32_t(slot_of(pages, p, page_size, ring_len));
+    return CB_OK;
+}
+
+extern "C" cb_status cb_validate_metadata(const int32_t *qsl, const int32_t *seq_lens, int32_t N,
+                                          const int32_t *table, int32_t width, const int32_t *ring_len,
+                                          const int32_t *slots, int32_t T, int32_t num_pages, int32_t P,
+                                          int32_t n_reserved, int32_t *bad_what, int32_t *bad_index) {
+    auto fail = [&](int32_t what, int64_t index) {
+        if (bad_what) *bad_what = what;
+        if (bad_index) *bad_index = int32_t(index);
+        return CB_E_INVAL;
+    };
+    if (bad_what) *bad_what = 0;
+    if (bad_index) *bad_index = -1;
+    if (N < 0 || T < 0 || width < 0 || num_pages < 1 || P < 1 || n_reserved < 0) return fail(0, -1);
+    if (!qsl || (N > 0 && (!seq_lens || (width > 0 && !table)))) return fail(0, -1);
+    if (qsl[0] != 0) return fail(1, 0);
+    for (int32_t r = 0; r < N; ++r)
+        if (qsl[r + 1] < qsl[r]) return fail(1, r + 1);
+    if (qsl[N] != T) return fail(1, N);
+    for (int32_t r = 0; r < N; ++r) {
+        const int32_t q = qsl[r + 1] - qsl[r];
+        if (seq_lens[r] < q) return fail(2, r);
+        const int32_t R = ring_len ? ring_len[r] : 0;
+        if (R < 0) return fail(3, r);
+        const int64_t used = R > 0 ? R : ceil_div(seq_lens[r], P);
+        if (used > width) return fail(3, r);
+        const int32_t *row = table + int64_t(r) * width;
+        for (int64_t b = 0; b < used; ++b)
+            if (row[b] < n_reserved || row[b] >= num_pages) return fail(3, r);
+        if (!slots) continue;
+        const int64_t ctx = int64_t(seq_lens[r]) - q;
+        for (int32_t j = 0; j < q; ++j) {
+            const int32_t s = slots[qsl[r] + j];
+            if (s >= 0 && s != slot_of(row, ctx + j, P, R)) return fail(4, qsl[r] + j);
+        }
+    }
+    return CB_OK;
 }
 
 // -------------------------------------------------------------------------------------------------- planner

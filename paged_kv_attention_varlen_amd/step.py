@@ -1,26 +1,23 @@
 """Device driver for one mixed step: metadata -> plans -> one host-to-device copy -> KV append -> attention.
 
-`Step` strings the library's calls together for one or two layer types (a full layer, optionally a sliding layer)
-that share the step's schedule. `Step.from_workload` builds the device state of a seeded synthetic workload: the
-KV caches (every page first filled with NaN, so pages that must never be read poison any output that reads them),
-the history of every admitted request written through cb_kv_append, and the step's new Q/K/V rows.
-
-History convention (setup, not part of the method): full layers get positions 0 .. context-1; sliding layers get
-only the positions this step's queries can still see, max(0, context - window_left) .. context-1, so older ring
-slots stay NaN.
+`Step` holds the device state of one scheduled step for one or two layer types (a full layer, optionally a sliding
+layer) that share the step's schedule: per layer the caches, the step's new Q/K/V rows, the output, the plan and its
+device copy, and the workspace. `StepPipeline` runs such a step again and again the way a serving loop does, every
+host and device stage included each time. Neither knows where the tensors' contents came from.
 """
 from __future__ import annotations
 
 import ctypes as C
-from concurrent.futures import ThreadPoolExecutor
+from collections import OrderedDict
 from dataclasses import dataclass
 from typing import List, Optional
 
 import numpy as np
 
 from .hip_events import HipEvent
-from . import (CB_PHASE_COMBINE, CB_PHASE_DECODE, CB_PHASE_PREFILL, CB_PHASE_ROWWISE, AttnPlan, CbError, _abi,
-               build_metadata, kv_append, paged_attention, plan_attention, workspace_size)
+from . import (CB_LAYOUT_KD_VT, CB_PHASE_COMBINE, CB_PHASE_DECODE, CB_PHASE_PREFILL, CB_PHASE_ROWWISE, AttnPlan,
+               CB_E_CAPACITY, CbError, Scheduler, _abi, check_dtypes, kv_append, paged_attention, plan_into,
+               schedule_arrays)
 
 
 def _torch():
@@ -79,170 +76,82 @@ class Step:
     PHASE_DECODE = CB_PHASE_DECODE
     PHASE_REST = CB_PHASE_ROWWISE | CB_PHASE_PREFILL | CB_PHASE_COMBINE
 
-    # ------------------------------------------------------------------------------------------- construction
-    @classmethod
-    def from_workload(cls, w, device: str = "cuda", decode_split: int = 0, prefill_split: int = 0,
-                      threads: int = 8, verbose: bool = False) -> "Step":
-        torch = _torch()
-        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-        P, Hq, Hkv, D = w.page_size, w.Hq, w.Hkv, w.D
-        pools = [{"ring_len": lay.ring_len, "window_left": lay.window_left,
-                  "pool_pages": lay.num_pages - len(lay.padding_pages), "free_pages": lay.free_pages}
-                 for lay in w.layers]
-        pad = w.layers[0].padding_pages[0] if w.layers[0].padding_pages else 0
-        sched = build_metadata(w.requests, pools, w.max_batch_tokens, w.max_requests, P, w.safety_margin, pad,
-                               policy=w.policy)
-        if sched["status"] != 0:
-            raise RuntimeError(f"cb_build_metadata returned status {sched['status']}")
-        N, T = sched["num_reqs"], sched["num_tokens"]
-        qsl, seq, idx = sched["query_start_loc"], sched["seq_lens"], sched["req_index"]
 
-        # one packed int32 host buffer -> one H2D copy: per layer block table, slot mapping, plan
-        plans, parts = [], []
-        for l, lay in enumerate(w.layers):
-            L = sched["layers"][l]
-            ring = L["ring_len"] if lay.ring_len > 0 else None
-            plan = plan_attention(qsl, seq, ring, Hq, Hkv, D, P, dt, lay.window_left, decode_split, prefill_split)
-            plans.append(plan)
-            parts += [L["block_table"].reshape(-1), L["slot_mapping"], plan.buffer]
-        offs = np.cumsum([0] + [p.size for p in parts])
-        packed = torch.from_numpy(np.concatenate(parts).astype(np.int32)).to(device)
-
-        def view(k, shape=None):
-            t = packed[offs[k]:offs[k + 1]]
-            return t.view(*shape) if shape is not None else t
-
-        layers = []
-        pool = ThreadPoolExecutor(max(1, threads))
-        for l, lay in enumerate(w.layers):
-            L = sched["layers"][l]
-            kc = torch.full((lay.num_pages, Hkv, P, D), float("nan"), dtype=dt, device=device)
-            vc = torch.full((lay.num_pages, Hkv, D, P), float("nan"), dtype=dt, device=device)
-            _fill_history(w, l, kc, vc, pool, device, dt)
-            q = torch.empty((T, Hq, D), dtype=dt)
-            kn = torch.empty((T, Hkv, D), dtype=dt)
-            vn = torch.empty((T, Hkv, D), dtype=dt)
-
-            def new_rows(r):
-                qs, qe = int(qsl[r]), int(qsl[r + 1])
-                ctx = int(seq[r]) - (qe - qs)
-                i = int(idx[r])
-                return qs, qe, [w.values(n, i, l, ctx, ctx + qe - qs) for n in ("q", "k", "v")]
-
-            for qs, qe, (a, b, c) in pool.map(new_rows, range(N)):
-                q[qs:qe] = torch.from_numpy(a).to(dt)
-                kn[qs:qe] = torch.from_numpy(b).to(dt)
-                vn[qs:qe] = torch.from_numpy(c).to(dt)
-            plan = plans[l]
-            ws_bytes = workspace_size(plan)
-            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device) if ws_bytes else None
-            layers.append(LayerState(lay.name, lay.window_left, lay.ring_len > 0, kc, vc, plan,
-                                     view(3 * l + 2), view(3 * l, (N, L["width"])), view(3 * l + 1),
-                                     q.to(device), kn.to(device), vn.to(device),
-                                     torch.empty((T, Hq, D), dtype=dt, device=device), ws))
-            if verbose:
-                print(f"[step] layer {lay.name}: plan {plan.counts()}", flush=True)
-        pool.shutdown()
-        torch.cuda.synchronize()
-        return cls(sched, layers, w.scale, dt, Hq, Hkv, D, P)
+def _roundup(x: int, m: int) -> int:
+    return -(-int(x) // m) * m if m > 1 else int(x)
 
 
-def history_slots(pages: np.ndarray, lo: int, hi: int, P: int, ring_len: int) -> np.ndarray:
-    """Cache slots (page * P + offset) of positions lo .. hi-1 of a request owning `pages` (logical order, or a
-    ring of ring_len pages)."""
-    pos = np.arange(lo, hi, dtype=np.int64)
-    blk = pos // P
-    if ring_len > 0:
-        blk = blk % ring_len
-    return (pages.astype(np.int64)[blk] * P + pos % P).astype(np.int32)
+class _Full(Exception):
+    """The padded metadata of a step does not fit the pipeline's buffers (they are then doubled), or its padded plan
+    needs more workspace than layer `layer` holds."""
 
-
-def _fill_history(w, l: int, kc, vc, pool, device, dt, chunk_tokens: int = 1 << 18) -> None:
-    """Write every admitted request's history into layer l's caches through cb_kv_append."""
-    torch = _torch()
-    lay = w.layers[l]
-    P = w.page_size
-    jobs = []
-    for i, rq in enumerate(w.requests):
-        if rq.num_computed == 0 or len(rq.pages[l]) == 0:
-            continue
-        lo = 0 if lay.window_left < 0 else max(0, rq.num_computed - lay.window_left)
-        jobs.append((i, lo, rq.num_computed))
-
-    def gen(job):
-        i, lo, hi = job
-        k = w.values("k", i, l, lo, hi)
-        v = w.values("v", i, l, lo, hi)
-        s = history_slots(np.asarray(w.requests[i].pages[l]), lo, hi, P, lay.ring_len)
-        return torch.from_numpy(k).to(dt), torch.from_numpy(v).to(dt), torch.from_numpy(s)
-
-    batch, n = [], 0
-
-    def flush():
-        nonlocal batch, n
-        if not batch:
-            return
-        k = torch.cat([b[0] for b in batch]).to(device)
-        v = torch.cat([b[1] for b in batch]).to(device)
-        s = torch.cat([b[2] for b in batch]).to(device)
-        kv_append(kc, vc, k, v, s)
-        batch, n = [], 0
-
-    group = 16   # requests generated ahead of the copies, bounding host memory
-    for g0 in range(0, len(jobs), group):
-        for res in pool.map(gen, jobs[g0:g0 + group]):
-            batch.append(res)
-            n += res[0].shape[0]
-            if n >= chunk_tokens:
-                flush()
-    flush()
+    def __init__(self, layer=None, need=0):
+        super().__init__()
+        self.layer, self.need = layer, need
 
 
 class StepPipeline:
-    """Runs a step again and again the way a serving loop would, every stage included each time.
+    """Runs steps the way a serving loop does, every host and device stage included each time.
 
-    Per step: the host schedules (cb_build_metadata) and plans every layer (cb_plan_attention) straight into a
-    pinned int32 buffer, which one asynchronous copy moves to the device; two host/device buffer pairs alternate,
-    so the host prepares step k+1 while the device still runs step k (the double-buffered async batching of the
-    Transformers "continuous batching architecture" page). Then, in stream order: the KV append of every layer,
-    the split-KV decode kernel, the prefill-tile and per-token kernels, and the merge of split rows.
+    Per step: the host schedules (cb_build_metadata, through `scheduler`, whose requests and free lists the caller
+    may replace between steps with Scheduler.set_state) and plans every layer (cb_plan_attention) into a pinned int32
+    buffer, which one asynchronous copy moves to the device; two host/device buffer pairs alternate, so the host
+    prepares step k+1 while the device still runs step k (the double-buffered async batching of the Transformers
+    "continuous batching architecture" page). Then, in stream order: the KV append of every layer, the split-KV
+    decode kernel, the prefill-tile and per-token kernels, and the merge of split rows. The step's new Q/K/V rows are
+    read from `step`'s tensors (row t = token t of the step), which the caller fills before `run`, in stream order on
+    the compute stream; they must have a row per token.
 
     concurrent=True runs the prefill-tile and per-token kernels on a second compute stream beside the decode kernel
-    (decode streams HBM while prefill keeps the matrix cores busy) and joins both before the merge. copy_stream=True
-    moves the metadata copy to a stream of its own, so that it overlaps the previous step's kernels instead of
-    sitting between steps. graphs=True replays the step's kernels as a captured HIP graph whenever the step's launch
-    configuration (metadata buffer, plans, token count) was seen before. fused_append=True (the default, except with
-    concurrent=True, whose prefill kernels would race the append) has cb_paged_attention write the new K/V itself:
-    the append's work groups run after the decode work groups in the decode launch, in the decode kernel's tail,
-    instead of in a launch of their own. All streams have the default priority.
+    and joins both before the merge. copy_stream=True moves the metadata copy to a stream of its own, so that it
+    overlaps the previous step's kernels instead of sitting between steps. fused_append=True (the default, except
+    with concurrent=True, whose prefill kernels would race the append) has cb_paged_attention write the new K/V
+    itself: the append's work groups run after the decode work groups in the decode launch. All streams have the
+    default priority.
+
+    graphs=True replays the step's kernels as captured HIP graphs keyed by a padded shape (same page, section "CUDA
+    图"): the token count is padded to a multiple of q_interval, every full layer's block-table width to a multiple of
+    kv_interval tokens, the block-table rows to a multiple of 16, and each section of every plan (decode, prefill,
+    per-token and merge items) and its count of split slots (which fixes the workspace layout) to a multiple of
+    item_interval. The metadata is then written at addresses that depend
+    only on the padded shape, the launches are sized for its capacities, and the kernels read the step's actual item
+    counts from the device buffer (the `counts` argument of cb_paged_attention), so one graph serves every step that
+    pads to the same shape. Padded tokens write their (unused) K/V rows into the reserved padding page, whose
+    contents are never read as valid keys (same page, section "内存管理"). At most max_graphs graphs are kept, the
+    least recently used evicted first.
     """
 
-    def __init__(self, w, step: Step, decode_split: int = 0, prefill_split: int = 0, concurrent: bool = False,
-                 copy_stream: bool = True, graphs: bool = False, fused_append: bool = True):
-        from . import Scheduler
+    def __init__(self, step: Step, scheduler: Scheduler, decode_split: int = 0, prefill_split: int = 0,
+                 concurrent: bool = False, copy_stream: bool = True, graphs: bool = False, fused_append: bool = True,
+                 q_interval: int = 64, kv_interval: int = 256, item_interval: int = 64, max_graphs: int = 8):
         torch = _torch()
         self.step = step
-        self.w = w
+        self.sched = scheduler
         self.concurrent = concurrent
         self.fused = fused_append and not concurrent
-        pools = [{"ring_len": lay.ring_len, "window_left": lay.window_left,
-                  "pool_pages": lay.num_pages - len(lay.padding_pages), "free_pages": lay.free_pages}
-                 for lay in w.layers]
-        pad = w.layers[0].padding_pages[0] if w.layers[0].padding_pages else 0
-        self.sched = Scheduler(w.requests, pools, w.max_batch_tokens, w.max_requests, w.page_size, w.safety_margin,
-                               pad, policy=w.policy)
-        dt = _abi.CB_DTYPE_BF16 if w.dtype == "bf16" else _abi.CB_DTYPE_F32
-        self.shapes = [_abi.cb_attn_shape(w.Hq, w.Hkv, w.D, w.page_size, dt, lay.window_left, decode_split,
-                                          prefill_split) for lay in w.layers]
-        # capacity: the one-off Step already built this schedule and these plans
-        meta = 8 * (step.sched["num_tokens"] + 4 * step.sched["num_reqs"] + 64) + sum(
-            L["block_table"].size for L in step.sched["layers"])
-        plan = sum(L.plan.buffer.size for L in step.layers)
-        self.meta_cap = int(meta)
-        self.cap = int(meta + 2 * plan + 1024)
-        dev = step.layers[0].out.device
-        self.host = [torch.empty(self.cap, dtype=torch.int32, pin_memory=True) for _ in range(2)]
-        self.dev = [torch.empty(self.cap, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.P = step.P
+        self.n_layers = len(step.layers)
+        if scheduler.L != self.n_layers or scheduler.page_size != step.P:
+            raise ValueError("scheduler and step disagree on layers or page size")
+        dt = _abi.CB_DTYPE_BF16 if str(step.dtype) == "torch.bfloat16" else _abi.CB_DTYPE_F32
+        self.dtype = dt
+        self.shapes = [_abi.cb_attn_shape(step.Hq, step.Hkv, step.D, step.P, dt, scheduler.windows[l], decode_split,
+                                          prefill_split) for l in range(self.n_layers)]
+        for L in step.layers:
+            check_dtypes(AttnPlan(None, self.shapes[0], None), q=L.q, out=L.out, k_cache=L.k_cache,
+                         v_cache=L.v_cache, k_new=L.k_new, v_new=L.v_new)
+        self.rows = min(L.q.shape[0] for L in step.layers)          # token capacity of the step's tensors
+        self.use_graphs = graphs
+        self.qi, self.kvi, self.ii = int(q_interval), int(kv_interval), int(item_interval)
+        self.max_graphs = int(max_graphs)
+        # buffer sizes start from the step the tensors were built for and double whenever a step needs more
+        self.meta_cap = int(2 * (4 * step.sched["num_reqs"] + step.sched["num_tokens"] * self.n_layers + 64 + sum(
+            Ls["block_table"].size + Ls["ring_len"].size for Ls in step.sched["layers"])) + 4096)
+        self.plan_cap = int(2 * sum(L.plan.buffer.size for L in step.layers) + 4096)
+        self.device = step.layers[0].out.device
+        self.graphs = OrderedDict()
+        self._alloc()
+        dev = self.device
         self.main = torch.cuda.current_stream(dev)
         self.aux = torch.cuda.Stream(dev) if concurrent else None
         self.copier = torch.cuda.Stream(dev) if copy_stream else None
@@ -267,40 +176,184 @@ class StepPipeline:
             a = _abi.cb_attn_args()
             a.out, a.q = L.out.data_ptr(), L.q.data_ptr()
             a.k_cache, a.v_cache = L.k_cache.data_ptr(), L.v_cache.data_ptr()
+            a.layout = CB_LAYOUT_KD_VT
             a.shape = self.shapes[l]
             a.num_pages = L.k_cache.shape[0]
             a.scale = float(step.scale)
             a.workspace = L.workspace.data_ptr() if L.workspace is not None else None
             a.workspace_bytes = L.workspace.numel() if L.workspace is not None else 0
             self.args.append(a)
+        self.workspaces = [L.workspace for L in step.layers]
+        self.ws_fits = [0] * self.n_layers     # split slots each layer's workspace is known to hold
         self.append_args = [(L.k_cache.data_ptr(), L.v_cache.data_ptr(), L.k_new.data_ptr(), L.v_new.data_ptr(),
-                             L.k_cache.shape[0], L.k_new.shape[0]) for L in step.layers]
-        self.dtype = dt
-        self.use_graphs = graphs
-        self.graphs = {}
+                             L.k_cache.shape[0]) for L in step.layers]
+        self.captures = 0          # graphs captured so far (evicted ones included)
+        self.replays = 0
+        self.key = None
+        self.last_header = None    # cb_step header of the last prepared step
+        self.last_plans = None     # its per-layer plan headers
+        self.keep_schedule = False  # True: prepare() also keeps the step's metadata as numpy arrays (last_schedule)
+        self.last_schedule = None
 
-    def prepare(self):
-        """Host half of a step: schedule + plan into the next pinned buffer and enqueue its copy to the device on
-        the compute stream (stream order keeps it after the previous step's kernels that read that buffer).
-        Returns the per-layer device views."""
+    # ---------------------------------------------------------------------------------------------- host half
+    def _alloc(self):
+        """(Re)allocate the two pinned / device buffer pairs: [scheduler output | plans | padded metadata]."""
         torch = _torch()
-        from . import plan_into
-        i = self.k % 2
-        self.k += 1
-        if self.copied[i] is not None:
-            self.copied[i].synchronize()   # the pinned half of pair i is free again
+        pad_cap = 2 * self.meta_cap + 2 * self.plan_cap + 64 * self.n_layers if self.use_graphs else 0
+        self.cap = self.meta_cap + self.plan_cap + pad_cap
+        self.host = [torch.empty(self.cap, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.dev = [torch.empty(self.cap, dtype=torch.int32, device=self.device) for _ in range(2)]
+        self.graphs.clear()    # captured launches point into the old buffers
+
+    def _grow(self):
+        torch = _torch()
+        torch.cuda.synchronize(self.device)
+        self.meta_cap *= 2
+        self.plan_cap *= 2
+        self._alloc()
+        self.copied = [None, None]
+        self.released = [None, None]
+
+    def _grow_workspace(self, l, need):
+        """Give layer l a workspace of at least `need` bytes (twice that, so that growth stays rare). The pipeline
+        owns it from then on; captured graphs point at the old one and are dropped."""
+        torch = _torch()
+        torch.cuda.synchronize(self.device)
+        ws = torch.empty(2 * need, dtype=torch.uint8, device=self.device)
+        self.workspaces[l] = ws
+        self.ws_fits[l] = 0
+        self.args[l].workspace, self.args[l].workspace_bytes = ws.data_ptr(), ws.numel()
+        self.graphs.clear()
+
+    def _check_workspace(self, l, info):
+        """Raise _Full(l, bytes) if layer l's workspace is too small for a plan with info's split slots."""
+        if info.n_partials <= self.ws_fits[l]:
+            return
+        probe = _abi.cb_attn_args()
+        probe.plan_info, probe.shape = info, self.shapes[l]
+        need = int(self.lib.cb_paged_attention_workspace_size(C.byref(probe)))
+        if need > self.args[l].workspace_bytes:
+            raise _Full(l, need)
+        self.ws_fits[l] = info.n_partials
+
+    def _host_step(self, i):
+        """Schedule and plan into pinned buffer i; with graphs=True also lay the metadata out at its padded shape.
+        Returns (header, plans, copy range lo, hi, launch views, graph key)."""
         host = self.host[i].numpy()
         hs = self.sched.build_into(host[:self.meta_cap])
         N, T = hs.num_reqs, hs.num_tokens
+        if T > self.rows:
+            raise ValueError(f"step has {T} tokens, the step's tensors hold {self.rows}")
         qsl = host[hs.off_query_start_loc:hs.off_query_start_loc + N + 1]
         seq = host[hs.off_seq_lens:hs.off_seq_lens + N]
-        at = int(hs.used)
+        plan_area = host[self.meta_cap:self.meta_cap + self.plan_cap]
+        at = 0
         plans = []
-        for l, lay in enumerate(self.w.layers):
-            ring = host[hs.off_ring_len[l]:hs.off_ring_len[l] + N] if lay.ring_len > 0 else None
-            p = plan_into(qsl, seq, ring, self.shapes[l], host[at:])
-            plans.append((p, at))
+        for l in range(self.n_layers):
+            ring = host[hs.off_ring_len[l]:hs.off_ring_len[l] + N] if self.sched.rings[l] > 0 else None
+            p = plan_into(qsl, seq, ring, self.shapes[l], plan_area[at:])
+            plans.append((p, self.meta_cap + at))
             at += int(p.info.used)
+        if self.use_graphs:
+            return (hs, plans) + self._pad(host, hs, plans, i)
+        for l, (p, _) in enumerate(plans):
+            self._check_workspace(l, p.info)
+        base = self.dev[i].data_ptr()
+        views = [(base + 4 * int(hs.off_block_table[l]), int(hs.table_width[l]),
+                  base + 4 * int(hs.off_slot_mapping[l]), p.info, base + 4 * off, None, T)
+                 for l, (p, off) in enumerate(plans)]
+        return hs, plans, 0, self.meta_cap + at, views, None
+
+    def _pad(self, host, hs, plans, i):
+        """Write the step's metadata at the addresses of its padded shape (see the class docstring): per layer the
+        block table, the slot mapping (padded tokens point into the padding page), the actual item counts, and the
+        plan with every section at its capacity. Returns (copy range lo, hi, launch views, graph key)."""
+        N, T = hs.num_reqs, hs.num_tokens
+        P = self.P
+        Tp = min(_roundup(max(T, 1), self.qi), self.rows)
+        Np = _roundup(max(N, 1), 16)
+        widths, caps = [], []
+        for l, (p, _) in enumerate(plans):
+            w = int(hs.table_width[l])
+            wp = w if self.sched.rings[l] > 0 else _roundup(max(w, 1), max(1, self.kvi // P))
+            widths.append(wp)
+            info = p.info
+            # n_partials sets where the workspace's second region (split maxima and sums) starts, so it is padded
+            # and keyed like the item counts
+            caps.append(tuple(_roundup(x, self.ii) for x in (info.n_decode, info.n_prefill, info.n_rowwise,
+                                                             info.n_combine, info.n_partials)))
+        at = lo = self.meta_cap + self.plan_cap
+        need = at + sum(Np * wp + Tp + 8 + 8 * sum(c[:3]) + 4 * c[3] for wp, c in zip(widths, caps))
+
+        if need > self.cap:
+            raise _Full()
+        base = self.dev[i].data_ptr()
+        views = []
+        for l, (p, poff) in enumerate(plans):
+            w, wp = int(hs.table_width[l]), widths[l]
+            bt = host[at:at + Np * wp].reshape(Np, wp)
+            bt[:] = self.sched.pad_page
+            if N and w:
+                bt[:N, :w] = host[hs.off_block_table[l]:hs.off_block_table[l] + N * w].reshape(N, w)
+            bt_at = at
+            at += Np * wp
+            sm = host[at:at + Tp]
+            sm[:T] = host[hs.off_slot_mapping[l]:hs.off_slot_mapping[l] + T]
+            sm[T:] = self.sched.pad_page * P + (np.arange(Tp - T) % P)
+            sm_at = at
+            at += Tp
+            info = p.info
+            cnt = host[at:at + 8]
+            cnt[:] = 0
+            cnt[:4] = (info.n_decode, info.n_prefill, info.n_rowwise, info.n_combine)
+            cnt_at = at
+            at += 8
+            src = host[poff:poff + int(info.used)]
+            padded = _abi.cb_plan()
+            C.memmove(C.byref(padded), C.byref(info), C.sizeof(padded))
+            pl_at = at
+            offs = []
+            for n, off, width, cap in ((info.n_decode, info.off_decode, 8, caps[l][0]),
+                                       (info.n_prefill, info.off_prefill, 8, caps[l][1]),
+                                       (info.n_rowwise, info.off_rowwise, 8, caps[l][2]),
+                                       (info.n_combine, info.off_combine, 4, caps[l][3])):
+                offs.append(at - pl_at)
+                host[at:at + n * width] = src[off:off + n * width]
+                at += cap * width
+            padded.n_decode, padded.n_prefill, padded.n_rowwise, padded.n_combine, padded.n_partials = caps[l]
+            padded.off_decode, padded.off_prefill, padded.off_rowwise, padded.off_combine = offs
+            padded.used = at - pl_at
+            padded.num_tokens = Tp
+            self._check_workspace(l, padded)
+            views.append((base + 4 * bt_at, wp, base + 4 * sm_at, padded, base + 4 * pl_at, base + 4 * cnt_at, Tp))
+        return lo, at, views, (i, Tp, Np, tuple(widths), tuple(caps))
+
+    def prepare(self):
+        """Host half of a step: schedule + plan into the next pinned buffer and enqueue its copy to the device.
+        Returns the per-layer launch views (block table, width, slot mapping, plan header, plan, counts, tokens)."""
+        torch = _torch()
+        i = self.k % 2
+        if self.copied[i] is not None:
+            self.copied[i].synchronize()   # the pinned half of pair i is free again
+        while True:
+            try:
+                hs, plans, lo, hi, views, key = self._host_step(i)
+                break
+            except CbError as e:
+                if e.status != CB_E_CAPACITY:
+                    raise
+                self._grow()
+            except _Full as e:
+                if e.layer is None:
+                    self._grow()
+                else:
+                    self._grow_workspace(e.layer, e.need)
+        self.k += 1
+        self.last_header = hs
+        self.last_plans = [p.info for p, _ in plans]
+        if self.keep_schedule:
+            self.last_schedule = schedule_arrays(self.host[i].numpy(), hs, self.n_layers)
+        self.num_tokens = hs.num_tokens
         dev = self.dev[i]
         ev = self.copy_ev[i]
         if self.copier is not None:
@@ -309,47 +362,40 @@ class StepPipeline:
             if self.released[i] is not None:
                 self.released[i].wait(self.copier)
             with torch.cuda.stream(self.copier):
-                dev[:at].copy_(self.host[i][:at], non_blocking=True)
+                dev[lo:hi].copy_(self.host[i][lo:hi], non_blocking=True)
             ev.record(self.copier)
             self.main.wait_event(ev)
         else:
-            dev[:at].copy_(self.host[i][:at], non_blocking=True)
+            dev[lo:hi].copy_(self.host[i][lo:hi], non_blocking=True)
             ev.record(self.main)
         self.copied[i] = ev
         self.cur = i
-        base = dev.data_ptr()
-        views = []
-        for l in range(len(self.w.layers)):
-            p, off = plans[l]
-            views.append((base + 4 * int(hs.off_block_table[l]), int(hs.table_width[l]),
-                          base + 4 * int(hs.off_slot_mapping[l]), p.info, base + 4 * off))
-        self.num_tokens = T
+        self.key = key
         return views
 
     def _check(self, status, what):
         if status != 0:
             raise CbError(status, what)
 
+    # -------------------------------------------------------------------------------------------- device half
     def _launch(self, views, stream, handle, events=None):
         """Enqueue the step's kernels for the prepared metadata `views` on `stream` (C handle `handle`)."""
         lib = self.lib
-        w = self.w
-        T = self.num_tokens
-        for l, (bt, width, sm, info, plan) in enumerate(views):
-            kc, vc, kn, vn, n_pages, rows = self.append_args[l]
-            if T > rows:
-                raise ValueError("step has more new tokens than the pipeline's input rows")
+        st = self.step
+        for l, (bt, width, sm, info, plan, counts, T) in enumerate(views):
+            kc, vc, kn, vn, n_pages = self.append_args[l]
             a = self.args[l]
+            a.counts = counts
             if self.fused:
                 a.k_new, a.v_new, a.slot_mapping, a.num_new = kn, vn, sm, T
             else:
                 a.k_new = a.v_new = a.slot_mapping = None
                 a.num_new = 0
-                self._check(lib.cb_kv_append(kc, vc, kn, vn, sm, T, n_pages, w.page_size, w.Hkv, w.D, self.dtype,
-                                             handle), "cb_kv_append")
+                self._check(lib.cb_kv_append(kc, vc, kn, vn, sm, T, n_pages, self.P, st.Hkv, st.D, self.dtype,
+                                             CB_LAYOUT_KD_VT, handle), "cb_kv_append")
 
         def attend(l, phases, ev0=None, ev1=None, aux=False):
-            bt, width, sm, info, plan = views[l]
+            bt, width, sm, info, plan, counts, T = views[l]
             a = self.args[l]
             a.block_table, a.table_width, a.plan, a.plan_info, a.phases = bt, width, plan, info, phases
             s = self.aux if aux else stream
@@ -379,33 +425,41 @@ class StepPipeline:
             attend(l, CB_PHASE_COMBINE, E(l, 4), E(l, 5))
 
     def _graph_for(self, views):
-        """The step's kernels captured as a HIP graph, cached by everything their launches depend on: the metadata
-        buffer (its device address), the plans (item counts, split sizes, section offsets), the block-table width
-        and the token count. A step whose launch configuration was seen before replays its graph."""
+        """The step's kernels captured as a HIP graph for the step's padded shape (captured at its first use)."""
         torch = _torch()
-        key = (self.cur, self.num_tokens) + tuple(
-            (bt, width, sm, plan, bytes(info)) for (bt, width, sm, info, plan) in views)
-        g = self.graphs.get(key)
-        if g is None:
-            side = torch.cuda.Stream(self.main.device)
-            side.wait_stream(self.main)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.stream(side):
-                g.capture_begin()
-                self._launch(views, side, C.c_void_p(side.cuda_stream))
-                g.capture_end()
-            self.main.wait_stream(side)
-            self.graphs[key] = g
+        g = self.graphs.get(self.key)
+        if g is not None:
+            self.graphs.move_to_end(self.key)
+            return g
+        side = torch.cuda.Stream(self.main.device)
+        side.wait_stream(self.main)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            g.capture_begin()
+            self._launch(views, side, C.c_void_p(side.cuda_stream))
+            g.capture_end()
+        self.main.wait_stream(side)
+        self.graphs[self.key] = g
+        self.captures += 1
+        while len(self.graphs) > self.max_graphs:
+            self.graphs.popitem(last=False)
         return g
 
     def run(self, events=None):
-        """One full step. `events`, if given, holds per layer 6 timing events: decode start/end (compute stream),
-        prefill start/end (the stream running the prefill-tile and per-token kernels), merge start/end. With
-        graphs=True the step replays a captured graph, except when it carries events (then it runs eagerly)."""
-        views = self.prepare()
+        """One full step: prepare() then launch()."""
+        self.launch(self.prepare(), events)
+
+    def launch(self, views, events=None):
+        """The device half of a prepared step. A caller that writes the step's new Q/K/V rows after seeing its
+        schedule (keep_schedule) does so between prepare() and launch(), in stream order on the compute stream.
+        `events`, if given, holds per layer 6 timing events: decode start/end (compute stream), prefill start/end
+        (the stream running the prefill-tile and per-token kernels), merge start/end. With graphs=True the step
+        replays the graph of its padded shape (captured at the shape's first step), except when it carries events:
+        then the same padded launches run eagerly."""
         main = self.main
         if self.use_graphs and events is None and not self.concurrent:
             self._graph_for(views).replay()
+            self.replays += 1
         else:
             self._launch(views, main, self.h_main, events)
         if self.copier is not None:

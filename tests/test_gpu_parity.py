@@ -1,8 +1,10 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
 
-Reduced workloads are compared element by element on every output row and every cache page; the full-size
-workloads -- in the launch configuration the benchmark times -- on sampled rows and on the pages the step's append
-touched. Tolerances: fp32 max-abs 1e-5; bf16 max-abs 2e-2 and mean-abs 2e-3; append bit-exact.
+Reduced workloads are compared element by element on every output row and every cache page. At full size, in the
+launch configuration the benchmark times: every row and every touched page of the decode-only step, the mixed
+2048-token step and the large decode batch; for the hybrid layer pair, every row of every split prefill tile, three
+unsplit tiles, a strided sample and decode rows, plus every touched page. Tolerances: fp32 max-abs 1e-5; bf16
+max-abs 2e-2 and mean-abs 2e-3; append bit-exact.
 """
 import numpy as np
 import pytest
@@ -28,9 +30,9 @@ def torch_gpu():
 def _run(w, fused=False, **kw):
     """Build the step and run it: cb_kv_append then cb_paged_attention, or (fused) cb_paged_attention alone with the
     new K/V passed in, appending them itself."""
-    from paged_kv_attention_varlen_amd.step import Step
+    from harness import build_step
     print(f"[gpu] {w.name} fused={fused} {kw}", flush=True)
-    st = Step.from_workload(w, **kw)
+    st = build_step(w, **kw)
     st.run(fused_append=fused)
     import torch
     torch.cuda.synchronize()
@@ -71,20 +73,60 @@ def _sample_tokens(sched, rng, n_dec=12, per_chunk=6):
     return sorted(toks)
 
 
-@pytest.mark.parametrize("idx", [2, 3, 4, 5])
-def test_full_workload_sampled_rows(torch_gpu, idx):
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_full_workload_every_row_and_touched_page(torch_gpu, idx):
+    """The decode-only step, the mixed 2048-token step and the large decode batch at full size, in the launch
+    configuration the benchmark times (the append fused into the decode launch): every output row element by
+    element, and every page the step's append wrote, bit for bit."""
     w = make_workload(idx)
-    st = _run(w, fused=True)       # the benchmark's launches: the append fused into cb_paged_attention
-    rng = np.random.default_rng(100 + idx)
+    st = _run(w, fused=True)
     sched = R.schedule(w)
-    toks = _sample_tokens(sched, rng)
+    out = st.layers[0].out
+    assert bool(torch_gpu.isfinite(out.float()).all()), "non-finite output somewhere"
+    mx, mean = H.compare(w, st, 0, label=f"w{idx} full")
+    print(f"  all {sched['num_tokens']} rows: max {mx:.3g} mean {mean:.3g}", flush=True)
+    touched = sorted(set((sched["layers"][0]["slot_mapping"] // w.page_size).tolist()))
+    _check_pages(w, st, 0, touched)
+    print(f"  {len(touched)} touched pages bit-exact", flush=True)
+
+
+def _tile_rows(plan, qsl_tokens, want_split, limit=None):
+    """Token rows of prefill tiles: those cut into several key-range items (want_split) or not."""
+    items = plan.items("prefill")
+    count = {}
+    for it in items:
+        count[(int(it[1]), int(it[3]))] = count.get((int(it[1]), int(it[3])), 0) + 1
+    tiles = sorted(k for k, n in count.items() if (n > 1) == want_split)
+    if limit is not None and len(tiles) > limit:
+        pick = np.linspace(0, len(tiles) - 1, limit).round().astype(int)
+        tiles = [tiles[i] for i in pick]
+    return sorted({t0 + i for t0, qc in tiles for i in range(qc)}), len(tiles)
+
+
+def test_full_hybrid_pair_split_tiles_and_strided_rows(torch_gpu):
+    """The hybrid layer pair at full size (8192 tokens, both layers), as the benchmark runs it. Per layer: every row
+    of every prefill tile whose key range the plan cut into several items (their partial results go through the
+    merge), every row of three unsplit tiles (first, middle, last), a strided sample of all rows (every 61st token)
+    and 24 decode rows (longest, shortest, random); every page the append touched, bit for bit; and a finiteness
+    check of every output row (a read of a NaN-poisoned page would show)."""
+    w = make_workload(5)
+    st = _run(w, fused=True)
+    sched = R.schedule(w)
+    rng = np.random.default_rng(105)
+    T = sched["num_tokens"]
     for l in range(len(w.layers)):
         out = st.layers[l].out
         assert bool(torch_gpu.isfinite(out.float()).all()), "non-finite output somewhere"
-        mx, mean = H.compare(w, st, l, toks, label=f"w{idx} full layer {l}")
-        print(f"  layer {l}: {len(toks)} rows, max {mx:.3g} mean {mean:.3g}", flush=True)
-        touched = set((sched["layers"][l]["slot_mapping"] // w.page_size).tolist())
-        _check_pages(w, st, l, sorted(touched)[:64])
+        plan = st.layers[l].plan
+        split_rows, n_split = _tile_rows(plan, sched["query_start_loc"], True)
+        plain_rows, _ = _tile_rows(plan, sched["query_start_loc"], False, limit=3)
+        toks = set(split_rows) | set(plain_rows) | set(range(0, T, 61))
+        toks |= set(_sample_tokens(sched, rng, n_dec=22, per_chunk=0))
+        mx, mean = H.compare(w, st, l, sorted(toks), label=f"w5 full layer {l}")
+        print(f"  layer {l}: {len(toks)} rows ({n_split} split tiles, {len(split_rows)} of their rows), "
+              f"max {mx:.3g} mean {mean:.3g}", flush=True)
+        touched = sorted(set((sched["layers"][l]["slot_mapping"] // w.page_size).tolist()))
+        _check_pages(w, st, l, touched)
 
 
 def test_workload_1_matches_explicit_mask(torch_gpu):
@@ -204,11 +246,11 @@ def test_pipeline_steps_match_oracle(torch_gpu, mode):
     pages. The append is fused into cb_paged_attention except with concurrent prefill and in the separate-append
     mode; the per-phase mode launches each kernel of the step on its own call, between timing events, as the
     benchmark does for its sampled steps."""
-    from paged_kv_attention_varlen_amd.step import Step, StepPipeline
+    from harness import build_step, pipeline_for
     for idx in (3, 5):
         w = make_workload(idx, mini=True)
-        st = Step.from_workload(w)
-        pipe = StepPipeline(w, st, copy_stream=(mode != "copy on compute stream"),
+        st = build_step(w)
+        pipe = pipeline_for(w, st, copy_stream=(mode != "copy on compute stream"),
                             concurrent=(mode == "concurrent prefill"), graphs=(mode == "graph replay"),
                             fused_append=(mode != "separate append"))
         events = None
@@ -228,7 +270,7 @@ def test_pipeline_steps_match_oracle(torch_gpu, mode):
         for l in range(len(w.layers)):
             _check_pages(w, st, l)
         if mode == "graph replay":
-            assert len(pipe.graphs) == 2, "one graph per metadata buffer"
+            assert pipe.captures == 2 and pipe.replays == 5, "one graph per metadata buffer of the padded shape"
         if events is not None:   # the events bracketed the decode, prefill and merge launches of the last step
             for l in range(len(w.layers)):
                 for a, b in ((0, 1), (2, 3), (4, 5)):
