@@ -336,6 +336,20 @@ size_t cb_paged_attention_workspace_size(const cb_attn_args *args);
  */
 cb_status cb_paged_attention(const cb_attn_args *args, void *stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): cb_paged_attention with the workspace taken from a static device array of
+ * CB_NOALLOC_WORKSPACE_BYTES, one per device, which the library holds from the load of its code object until the
+ * process ends. args->workspace and args->workspace_bytes are ignored. The caller still passes every input and
+ * output. Allocates nothing (no hipMalloc / hipFree, no allocating library call). Returns CB_E_WORKSPACE, before any
+ * launch, if the plan's workspace (cb_paged_attention_workspace_size) exceeds the array; CB_E_INVAL if `stream`
+ * belongs to a device other than the current one; otherwise what cb_paged_attention returns. All calls on one
+ * device share its array: calls that overlap on one device (on different streams, or enqueued before an earlier
+ * one has finished reading its partial results) race.
+ */
+#define CB_NOALLOC_WORKSPACE_BYTES (96u << 20)
+cb_status cb_paged_attention_noalloc(const cb_attn_args *args, void *stream);
+
 /* ------------------------------------------------------------------------------------------------ prefix cache */
 
 /*

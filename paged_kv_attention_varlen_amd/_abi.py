@@ -15,6 +15,7 @@ CB_PHASE_DECODE, CB_PHASE_ROWWISE, CB_PHASE_PREFILL, CB_PHASE_COMBINE = 1, 2, 4,
 CB_POLICY_FIFO, CB_POLICY_PREFILL_FIRST = 0, 1
 ABI_VERSION = 4
 CB_LAYOUT_PAGED_NHD, CB_LAYOUT_KD_VT = 0, 1
+CB_NOALLOC_WORKSPACE_BYTES = 96 << 20
 
 i32p = C.POINTER(C.c_int32)
 
@@ -69,7 +70,7 @@ class cb_attn_args(C.Structure):
                 ("num_new", C.c_int32), ("counts", C.c_void_p)]
 
 
-EXPORTS = ("cb_build_metadata", "cb_slot_mapping", "cb_validate_metadata", "cb_plan_attention", "cb_kv_append", "cb_kv_copy_pages", "cb_paged_attention",
+EXPORTS = ("cb_build_metadata", "cb_slot_mapping", "cb_validate_metadata", "cb_plan_attention", "cb_kv_append", "cb_kv_copy_pages", "cb_paged_attention", "cb_paged_attention_noalloc",
            "cb_paged_attention_workspace_size", "cb_fnv1a64", "cb_block_hashes", "cb_pcache_create",
            "cb_pcache_destroy", "cb_pcache_match", "cb_pcache_allocate", "cb_pcache_commit", "cb_pcache_release",
            "cb_pcache_stats", "cb_pcache_page_info", "cb_status_str", "cb_abi_version")
@@ -111,6 +112,8 @@ def load(path: str = LIB_PATH):
                                      C.c_int64, C.c_void_p]
     lib.cb_paged_attention.restype = C.c_int32
     lib.cb_paged_attention.argtypes = [C.POINTER(cb_attn_args), C.c_void_p]
+    lib.cb_paged_attention_noalloc.restype = C.c_int32
+    lib.cb_paged_attention_noalloc.argtypes = [C.POINTER(cb_attn_args), C.c_void_p]
     lib.cb_paged_attention_workspace_size.restype = C.c_size_t
     lib.cb_paged_attention_workspace_size.argtypes = [C.POINTER(cb_attn_args)]
     u64p = C.POINTER(C.c_uint64)

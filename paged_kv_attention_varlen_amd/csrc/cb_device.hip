@@ -14,6 +14,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "cb.h"
 
@@ -1201,3 +1202,45 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
     return hipGetLastError() == hipSuccess ? CB_OK : CB_E_HIP;
 }
 
+// ============================================================================ allocation-free entry point
+//
+// The same launches as cb_paged_attention, with the partial results of split rows kept in `scratch`, a static
+// device array of fixed size: one copy per device, allocated when the code object is loaded and held until the
+// process ends. Host code never passes `scratch` itself to a kernel (in host code the name stands for a host-side
+// shadow, not a device address): its device address is taken once per device with hipGetSymbolAddress and kept
+// in g_scratch. Every split slot is written by the work group that owns it before the merge reads it, so nothing in
+// the array has to start at zero; two calls that overlap on one device share the array and race.
+
+static __device__ __align__(256) uint8_t scratch[CB_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];   // device address of `scratch` on each device, looked up at the first call there
+}  // namespace
+
+extern "C" cb_status cb_paged_attention_noalloc(const cb_attn_args *a, void *stream) {
+    if (!a) return CB_E_INVAL;
+    if (cb_paged_attention_workspace_size(a) > size_t(CB_NOALLOC_WORKSPACE_BYTES)) return CB_E_WORKSPACE;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CB_E_HIP;
+    if (stream) {   // the scratch address below is the current device's: the stream must belong to it
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) return CB_E_HIP;
+        if (int(sdev) != dev) return CB_E_INVAL;
+    }
+    void *ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_scratch[dev]) {
+            void *p = nullptr;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CB_E_HIP;
+            g_scratch[dev] = p;
+        }
+        ptr = g_scratch[dev];
+    }
+    cb_attn_args b = *a;
+    b.workspace = ptr;
+    b.workspace_bytes = size_t(CB_NOALLOC_WORKSPACE_BYTES);
+    return cb_paged_attention(&b, stream);
+}
