@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 4
+#define CB_ABI_VERSION 5
 
 typedef int32_t cb_status;
 #define CB_OK 0
@@ -70,6 +70,8 @@ typedef int32_t cb_status;
 
 /* ------------------------------------------------------------------------------------------- cb_build_metadata */
 
+typedef struct cb_prefix_cache cb_prefix_cache;   /* prefix cache (see "prefix cache" below), opaque */
+
 /* One request known to the scheduler, given in arrival (FIFO) order. */
 typedef struct cb_req {
     int64_t id;                          /* caller's id; not interpreted                                         */
@@ -78,6 +80,9 @@ typedef struct cb_req {
     int32_t num_pending;                 /* tokens to feed: exactly 1 for CB_DECODING, >= 1 otherwise            */
     int32_t n_pages[CB_MAX_LAYERS];      /* pages already owned per layer type                                   */
     const int32_t *pages[CB_MAX_LAYERS]; /* host arrays of owned page ids, logical order (full) or ring order    */
+    const uint64_t *prompt_hashes;       /* chain hashes of the prompt's full blocks (cb_block_hashes), or NULL:
+                                            looked up in the prefix cache when the request is admitted          */
+    int32_t n_prompt_blocks;             /* entries of prompt_hashes                                            */
 } cb_req;
 
 /* One layer type's page pool. */
@@ -103,6 +108,8 @@ typedef struct cb_sched_params {
     int32_t policy;            /* CB_POLICY_FIFO or CB_POLICY_PREFILL_FIRST                                     */
     float safety_margin;       /* hold new prefills while any pool's free fraction is below this (0 disables);
                                   the page gives 0.15 as the FIFO default and 0 for PrefillFirst              */
+    cb_prefix_cache *prefix_cache; /* NULL, or a prefix cache over layer 0's pool: prefix sharing at admission
+                                  (see cb_build_metadata)                                                      */
 } cb_sched_params;
 
 /* Header of the packed int32 buffer cb_build_metadata writes. Offsets count int32 elements from the buffer start;
@@ -116,6 +123,7 @@ typedef struct cb_step {
     int32_t n_stalled;                       /* active requests left out for lack of pages                       */
     int32_t first_rejected;                  /* input index of the waiting request refused admission, or -1      */
     int32_t held_by_margin;                  /* 1 if new prefills were held by the safety margin                 */
+    int32_t prefix_sharing;                  /* 1 if the step scheduled with prefix sharing on                   */
     int32_t used_pages[CB_MAX_LAYERS];       /* pages taken from the front of each free list                     */
     int32_t table_width[CB_MAX_LAYERS];      /* row stride of each layer's block table                           */
     int64_t off_query_start_loc;             /* [N+1]                                                            */
@@ -125,6 +133,7 @@ typedef struct cb_step {
     int64_t off_block_table[CB_MAX_LAYERS];  /* [N][table_width]; unused entries hold pad_page                   */
     int64_t off_slot_mapping[CB_MAX_LAYERS]; /* [T] page * page_size + offset of each new token's K/V            */
     int64_t off_ring_len[CB_MAX_LAYERS];     /* [N] ring length per row (0 for full layers)                      */
+    int64_t off_matched;                     /* [N] prompt tokens each row reused from the prefix cache          */
     int64_t used;                            /* int32 elements written, or needed when CB_E_CAPACITY            */
 } cb_step;
 
@@ -139,7 +148,23 @@ typedef struct cb_step {
  *      refusal stops admission.
  *   Every pass stops at max_requests rows or an exhausted budget, and takes its pages from the front of the free
  *   lists in that order. Active requests whose pages cannot be allocated are reported stalled and left out.
- * Pure host function: reads reqs/params/layers, writes `out` (capacity out_capacity int32 elements) and `step`.
+ * Prefix sharing (same page, sections "前缀缓存" and "准入"), when params->prefix_cache is set and the step has one
+ * layer type, a full-attention one (the page: sharing is on only when every allocator supports it, so sliding and
+ * hybrid models run without it; with a ring layer the cache is ignored):
+ *   - every page the step takes comes from the cache's allocator (cb_pcache_allocate order: empty pages first,
+ *     then demoted initialized ones), not from layers[0].free_pages;
+ *   - a waiting request with num_computed 0 and no pages first looks up the leading blocks of its prompt_hashes,
+ *     at most (num_pending - 1) / page_size of them, so that at least one prompt token is still computed; their
+ *     pages become its first pages (references taken) and its context starts at matched * page_size;
+ *   - admission stays all-or-nothing: the match is taken only if the fresh pages for the rest of the chunk can be
+ *     allocated too, counting matched pages that sat free in the cache as leaving its free pool;
+ *   - the safety margin and every availability check use the cache's free pages.
+ * The call then changes the cache (references taken, pages allocated); the caller registers completed prompt blocks
+ * (cb_pcache_commit) after the step and releases a finished request's pages. To keep a failed call from changing
+ * the cache, the output capacity is checked first against a bound of the output size (step->used = that bound on
+ * CB_E_CAPACITY).
+ * Without a prefix cache the call is a pure host function: reads reqs/params/layers, writes `out` (capacity
+ * out_capacity int32 elements) and `step`.
  * Returns CB_OK, CB_E_INVAL (inconsistent input, including a ring too small for max_batch_tokens), CB_E_NOSPACE
  * (no row could be scheduled because pages ran out; out/step are still valid) or CB_E_CAPACITY (step->used tells
  * the size needed).
@@ -361,7 +386,7 @@ cb_status cb_paged_attention_noalloc(const cb_attn_args *args, void *stream);
  * (its hash dropped). Host only, deterministic; page ids are the caller's pool (full-attention layers: the page says
  * sliding and hybrid models do not share). All functions return CB_E_INVAL on null or out-of-range arguments.
  */
-typedef struct cb_prefix_cache cb_prefix_cache;   /* opaque, owned by the library between create and destroy */
+/* cb_prefix_cache (declared at the top) is opaque, owned by the library between create and destroy. */
 
 /* FNV-1a 64-bit hash of n bytes (offset basis 14695981039346656037, prime 1099511628211). */
 uint64_t cb_fnv1a64(const void *data, int64_t n);
@@ -380,6 +405,12 @@ void cb_pcache_destroy(cb_prefix_cache *cache);
  * each gains a reference (a freed one comes back into use); *n_matched tells how many. */
 cb_status cb_pcache_match(cb_prefix_cache *cache, const uint64_t *hashes, int32_t n_blocks, int32_t *pages_out,
                           int32_t *n_matched);
+
+/* Pages of the leading registered blocks of hashes [n_blocks], into pages_out, WITHOUT taking references: *n_found
+ * tells how many, *n_free_found how many of those pages are currently free (initialized, no reference), i.e. would
+ * leave the free pool if matched. Either count pointer may be NULL. */
+cb_status cb_pcache_lookup(const cb_prefix_cache *cache, const uint64_t *hashes, int32_t n_blocks, int32_t *pages_out,
+                           int32_t *n_found, int32_t *n_free_found);
 
 /* n fresh pages with one reference each, into pages_out [n]: empty pages first, in free-list order, then demoted
  * initialized pages, most recently freed first. All or nothing: CB_E_NOSPACE, and nothing taken, if fewer exist. */

@@ -41,30 +41,44 @@ def _ptr(a: np.ndarray):
 
 # ------------------------------------------------------------------------------------------- cb_build_metadata
 
+def _marshal_requests(requests, L, prompt_hashes, keep):
+    n = len(requests)
+    reqs = (_abi.cb_req * max(n, 1))()
+    for i, rq in enumerate(requests):
+        r = reqs[i]
+        r.id, r.state, r.num_computed, r.num_pending = int(rq.id), int(rq.state), int(rq.num_computed), \
+            int(rq.num_pending)
+        for l in range(L):
+            p = _i32(rq.pages[l])
+            keep.append(p)
+            r.n_pages[l] = p.size
+            r.pages[l] = _ptr(p)
+        h = None if prompt_hashes is None else prompt_hashes[i]
+        if h is not None and len(h):
+            h = np.ascontiguousarray(np.asarray(h, dtype=np.uint64))
+            keep.append(h)
+            r.prompt_hashes = h.ctypes.data_as(C.POINTER(C.c_uint64))
+            r.n_prompt_blocks = h.size
+    return reqs
+
+
 def build_metadata(requests, layers, max_batch_tokens: int, max_requests: int, page_size: int,
-                   safety_margin: float = 0.0, pad_page: int = 0, policy: str = "fifo") -> dict:
+                   safety_margin: float = 0.0, pad_page: int = 0, policy: str = "fifo", prefix_cache=None,
+                   prompt_hashes=None) -> dict:
     """Schedule one step (cb_build_metadata). policy: "fifo" or "prefill_first".
 
     requests: sequence of objects with .id, .state (0 decoding / 1 prefilling / 2 waiting), .num_computed,
       .num_pending and .pages (one int array per layer), in arrival order.
     layers: sequence of dicts {ring_len, window_left, pool_pages, free_pages}.
+    prefix_cache: a PrefixCache for prefix sharing at admission, with prompt_hashes[i] the chain hashes of request
+      i's full prompt blocks (or None); the call then takes references in the cache.
     Returns a dict with "status" (int) and, unless the input was invalid, the metadata as numpy arrays.
     """
     lib = _abi.load()
     n = len(requests)
     L = len(layers)
     keep = []
-    reqs = (_abi.cb_req * max(n, 1))()
-    for i, rq in enumerate(requests):
-        reqs[i].id = int(rq.id)
-        reqs[i].state = int(rq.state)
-        reqs[i].num_computed = int(rq.num_computed)
-        reqs[i].num_pending = int(rq.num_pending)
-        for l in range(L):
-            p = _i32(rq.pages[l])
-            keep.append(p)
-            reqs[i].n_pages[l] = p.size
-            reqs[i].pages[l] = _ptr(p)
+    reqs = _marshal_requests(requests, L, prompt_hashes, keep)
     pools = (_abi.cb_layer_pool * max(L, 1))()
     for l, lay in enumerate(layers):
         f = _i32(lay["free_pages"])
@@ -75,7 +89,8 @@ def build_metadata(requests, layers, max_batch_tokens: int, max_requests: int, p
         pools[l].n_free = f.size
         pools[l].free_pages = _ptr(f)
     params = _abi.cb_sched_params(int(max_batch_tokens), int(max_requests), int(page_size), int(pad_page), L,
-                                  POLICIES[policy], float(safety_margin))
+                                  POLICIES[policy], float(safety_margin),
+                                  prefix_cache._h if prefix_cache is not None else None)
     step = _abi.cb_step()
     cap = 4096
     while True:
@@ -133,24 +148,36 @@ class Request:
     pages: list
 
 
-def advance(requests, schedule: dict, free_pages, ring_lens, page_size: int):
+def advance(requests, schedule: dict, free_pages, ring_lens, page_size: int, prefix_cache=None,
+            prompt_hashes=None):
     """Request lifecycle after a step has run (Transformers "continuous batching architecture" page, section
     "请求生命周期": a waiting request is admitted and prefilled in chunks, then decodes one token per step).
 
     schedule: the step's metadata as `build_metadata` returns it (query_start_loc, seq_lens, req_index and per layer
-    the block table and used_pages). Every scheduled request has now computed its q_len tokens: a request whose
-    prompt is done decodes next (one pending token: the one this step produced), otherwise it keeps prefilling; its
-    pages are its block-table row (ceil(seq_len / page_size) pages, or its whole ring). Pages the step took leave the
-    front of each free list. Requests the step did not schedule are unchanged. Returns (requests, free_pages) as new
-    lists (Request records in the input order)."""
+    the block table and used_pages). Every scheduled request has now computed its keys up to its seq_len (its
+    q_len tokens, plus any prompt tokens it reused from the prefix cache): a request whose prompt is done decodes
+    next (one pending token: the one this step produced), otherwise it keeps prefilling; its pages are its
+    block-table row (ceil(seq_len / page_size) pages, or its whole ring). Pages the step took leave the front of
+    each free list (unless the prefix cache allocated them). With a prefix cache, every prompt block the step
+    completed is registered under its hash (prompt_hashes[i], chain hashes of request i's full prompt blocks), so
+    that later requests can reuse it (same page, section "前缀缓存": every completed block is content-hashed).
+    Requests the step did not schedule are unchanged. Returns (requests, free_pages) as new lists (Request records
+    in the input order)."""
     qsl, seq, idx = schedule["query_start_loc"], schedule["seq_lens"], schedule["req_index"]
+    P = int(page_size)
     out = [Request(int(r.id), int(r.state), int(r.num_computed), int(r.num_pending),
                    [np.asarray(p, dtype=np.int32) for p in r.pages]) for r in requests]
     for row in range(len(idx)):
-        rq = out[int(idx[row])]
+        i = int(idx[row])
+        rq = out[i]
         q = int(qsl[row + 1] - qsl[row])
-        rq.num_computed += q
-        rq.num_pending -= q
+        ctx = int(seq[row]) - q
+        if prefix_cache is not None and prompt_hashes is not None and prompt_hashes[i] is not None:
+            table = schedule["layers"][0]["block_table"][row]
+            for b in range(ctx // P, min(int(seq[row]) // P, len(prompt_hashes[i]))):
+                prefix_cache.commit(int(table[b]), int(prompt_hashes[i][b]))
+        rq.num_pending -= int(seq[row]) - rq.num_computed
+        rq.num_computed = int(seq[row])
         if rq.num_pending <= 0:
             rq.state, rq.num_pending = CB_DECODING, 1
         else:
@@ -158,7 +185,8 @@ def advance(requests, schedule: dict, free_pages, ring_lens, page_size: int):
         for l, lay in enumerate(schedule["layers"]):
             n = int(ring_lens[l]) if ring_lens[l] > 0 else -(-int(seq[row]) // page_size)
             rq.pages[l] = np.array(lay["block_table"][row, :n], dtype=np.int32)
-    free = [np.asarray(f, dtype=np.int32)[int(lay["used_pages"]):].copy()
+    shared = schedule.get("prefix_sharing", False)
+    free = [np.asarray(f, dtype=np.int32)[0 if shared else int(lay["used_pages"]):].copy()
             for f, lay in zip(free_pages, schedule["layers"])]
     return out, free
 
@@ -173,7 +201,9 @@ def schedule_arrays(buf: np.ndarray, step, n_layers: int) -> dict:
          "seq_lens": buf[step.off_seq_lens:step.off_seq_lens + N].copy(),
          "req_index": buf[step.off_req_index:step.off_req_index + N].copy(),
          "stalled": buf[step.off_stalled:step.off_stalled + step.n_stalled].copy(),
-         "first_rejected": step.first_rejected, "held_by_margin": bool(step.held_by_margin), "layers": []}
+         "first_rejected": step.first_rejected, "held_by_margin": bool(step.held_by_margin), "layers": [],
+         "prefix_sharing": bool(step.prefix_sharing),
+         "matched_tokens": buf[step.off_matched:step.off_matched + N].copy()}
     for l in range(n_layers):
         w = step.table_width[l]
         bt = buf[step.off_block_table[l]:step.off_block_table[l] + N * w].reshape(N, w).copy()
@@ -189,8 +219,11 @@ class Scheduler:
     host memory that is then copied to the device in one transfer)."""
 
     def __init__(self, requests, layers, max_batch_tokens: int, max_requests: int, page_size: int,
-                 safety_margin: float = 0.0, pad_page: int = 0, policy: str = "fifo"):
+                 safety_margin: float = 0.0, pad_page: int = 0, policy: str = "fifo", prefix_cache=None,
+                 prompt_hashes=None):
         self._lib = _abi.load()
+        self.prefix_cache = prefix_cache
+        self.prompt_hashes = prompt_hashes
         self.L = len(layers)
         self.page_size = int(page_size)
         self.pad_page = int(pad_page)
@@ -199,7 +232,8 @@ class Scheduler:
         self.windows = [int(lay["window_left"]) for lay in layers]
         self.rings = [int(lay["ring_len"]) for lay in layers]
         self.params = _abi.cb_sched_params(int(max_batch_tokens), int(max_requests), int(page_size), int(pad_page),
-                                           self.L, POLICIES[policy], float(safety_margin))
+                                           self.L, POLICIES[policy], float(safety_margin),
+                                           prefix_cache._h if prefix_cache is not None else None)
         self.set_state(requests, [lay["free_pages"] for lay in layers], [int(lay["pool_pages"]) for lay in layers])
 
     def set_state(self, requests, free_pages, pool_pages=None) -> None:
@@ -210,16 +244,7 @@ class Scheduler:
         self.n = n
         self.requests = list(requests)
         self.free_pages = [np.asarray(f, dtype=np.int32) for f in free_pages]
-        reqs = (_abi.cb_req * max(n, 1))()
-        for i, rq in enumerate(requests):
-            r = reqs[i]
-            r.id, r.state, r.num_computed, r.num_pending = int(rq.id), int(rq.state), int(rq.num_computed), \
-                int(rq.num_pending)
-            for l in range(L):
-                p = _i32(rq.pages[l])
-                keep.append(p)
-                r.n_pages[l] = p.size
-                r.pages[l] = _ptr(p)
+        reqs = _marshal_requests(requests, L, self.prompt_hashes, keep)
         if pool_pages is None:
             pool_pages = [self.pools[l].pool_pages for l in range(L)]
         pools = (_abi.cb_layer_pool * max(L, 1))()
@@ -232,7 +257,8 @@ class Scheduler:
     def advance(self, schedule: dict) -> None:
         """After the step `schedule` has run: move every request along its lifecycle (`advance`) and drop the pages
         the step took from the free lists."""
-        reqs, free = advance(self.requests, schedule, self.free_pages, self.rings, self.page_size)
+        reqs, free = advance(self.requests, schedule, self.free_pages, self.rings, self.page_size, self.prefix_cache,
+                             self.prompt_hashes)
         self.set_state(reqs, free)
 
     def build_into(self, out: np.ndarray) -> _abi.cb_step:
@@ -414,6 +440,15 @@ class PrefixCache:
         self._call(self._lib.cb_pcache_match(self._h, hs.ctypes.data_as(C.POINTER(C.c_uint64)), hs.size, _ptr(out),
                                              C.byref(n)), "cb_pcache_match")
         return out[:n.value].copy()
+
+    def lookup(self, hashes):
+        """Pages of the leading registered blocks (no references taken) and how many of them are free."""
+        hs = np.ascontiguousarray(np.asarray(hashes, dtype=np.uint64))
+        out = np.zeros(max(hs.size, 1), dtype=np.int32)
+        n, nf = C.c_int32(), C.c_int32()
+        self._call(self._lib.cb_pcache_lookup(self._h, hs.ctypes.data_as(C.POINTER(C.c_uint64)), hs.size, _ptr(out),
+                                              C.byref(n), C.byref(nf)), "cb_pcache_lookup")
+        return out[:n.value].copy(), nf.value
 
     def allocate(self, n: int) -> np.ndarray:
         out = np.zeros(max(n, 1), dtype=np.int32)

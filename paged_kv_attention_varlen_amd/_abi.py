@@ -13,7 +13,7 @@ CB_DECODING, CB_PREFILLING, CB_WAITING = 0, 1, 2
 CB_MAX_LAYERS = 2
 CB_PHASE_DECODE, CB_PHASE_ROWWISE, CB_PHASE_PREFILL, CB_PHASE_COMBINE = 1, 2, 4, 8
 CB_POLICY_FIFO, CB_POLICY_PREFILL_FIRST = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 CB_LAYOUT_PAGED_NHD, CB_LAYOUT_KD_VT = 0, 1
 CB_NOALLOC_WORKSPACE_BYTES = 96 << 20
 
@@ -22,7 +22,8 @@ i32p = C.POINTER(C.c_int32)
 
 class cb_req(C.Structure):
     _fields_ = [("id", C.c_int64), ("state", C.c_int32), ("num_computed", C.c_int32), ("num_pending", C.c_int32),
-                ("n_pages", C.c_int32 * CB_MAX_LAYERS), ("pages", i32p * CB_MAX_LAYERS)]
+                ("n_pages", C.c_int32 * CB_MAX_LAYERS), ("pages", i32p * CB_MAX_LAYERS),
+                ("prompt_hashes", C.POINTER(C.c_uint64)), ("n_prompt_blocks", C.c_int32)]
 
 
 class cb_layer_pool(C.Structure):
@@ -33,18 +34,18 @@ class cb_layer_pool(C.Structure):
 class cb_sched_params(C.Structure):
     _fields_ = [("max_batch_tokens", C.c_int32), ("max_requests", C.c_int32), ("page_size", C.c_int32),
                 ("pad_page", C.c_int32), ("n_layers", C.c_int32), ("policy", C.c_int32),
-                ("safety_margin", C.c_float)]
+                ("safety_margin", C.c_float), ("prefix_cache", C.c_void_p)]
 
 
 class cb_step(C.Structure):
     _fields_ = [("num_reqs", C.c_int32), ("num_tokens", C.c_int32), ("num_decodes", C.c_int32),
                 ("max_q_len", C.c_int32), ("max_seq_len", C.c_int32), ("n_stalled", C.c_int32),
-                ("first_rejected", C.c_int32), ("held_by_margin", C.c_int32),
+                ("first_rejected", C.c_int32), ("held_by_margin", C.c_int32), ("prefix_sharing", C.c_int32),
                 ("used_pages", C.c_int32 * CB_MAX_LAYERS), ("table_width", C.c_int32 * CB_MAX_LAYERS),
                 ("off_query_start_loc", C.c_int64), ("off_seq_lens", C.c_int64), ("off_req_index", C.c_int64),
                 ("off_stalled", C.c_int64), ("off_block_table", C.c_int64 * CB_MAX_LAYERS),
                 ("off_slot_mapping", C.c_int64 * CB_MAX_LAYERS), ("off_ring_len", C.c_int64 * CB_MAX_LAYERS),
-                ("used", C.c_int64)]
+                ("off_matched", C.c_int64), ("used", C.c_int64)]
 
 
 class cb_attn_shape(C.Structure):
@@ -72,7 +73,7 @@ class cb_attn_args(C.Structure):
 
 EXPORTS = ("cb_build_metadata", "cb_slot_mapping", "cb_validate_metadata", "cb_plan_attention", "cb_kv_append", "cb_kv_copy_pages", "cb_paged_attention", "cb_paged_attention_noalloc",
            "cb_paged_attention_workspace_size", "cb_fnv1a64", "cb_block_hashes", "cb_pcache_create",
-           "cb_pcache_destroy", "cb_pcache_match", "cb_pcache_allocate", "cb_pcache_commit", "cb_pcache_release",
+           "cb_pcache_destroy", "cb_pcache_match", "cb_pcache_lookup", "cb_pcache_allocate", "cb_pcache_commit", "cb_pcache_release",
            "cb_pcache_stats", "cb_pcache_page_info", "cb_status_str", "cb_abi_version")
 
 _lib = None
@@ -127,6 +128,8 @@ def load(path: str = LIB_PATH):
     lib.cb_pcache_destroy.argtypes = [C.c_void_p]
     lib.cb_pcache_match.restype = C.c_int32
     lib.cb_pcache_match.argtypes = [C.c_void_p, u64p, C.c_int32, i32p, i32p]
+    lib.cb_pcache_lookup.restype = C.c_int32
+    lib.cb_pcache_lookup.argtypes = [C.c_void_p, u64p, C.c_int32, i32p, i32p, i32p]
     lib.cb_pcache_allocate.restype = C.c_int32
     lib.cb_pcache_allocate.argtypes = [C.c_void_p, C.c_int32, i32p]
     lib.cb_pcache_commit.restype = C.c_int32

@@ -1,7 +1,8 @@
 // Host half of the cb library: the step scheduler (cb_build_metadata) and the work planner (cb_plan_attention).
 //
-// Both are pure functions of their arguments: no allocation visible to the caller, no global state, no RNG.
-// Page allocation takes pages from the front of the caller's (already shuffled) free lists.
+// Both are functions of their arguments only: no allocation visible to the caller, no global state, no RNG. Page
+// allocation takes pages from the front of the caller's (already shuffled) free lists -- or, when the caller passes a
+// prefix cache, from that cache, whose references the scheduler then takes (the one state it changes).
 
 #include <algorithm>
 #include <cstdint>
@@ -34,8 +35,11 @@ inline int64_t slot_of(const int32_t *row, int64_t pos, int32_t P, int32_t ring_
 struct Scheduled {
     int32_t req;                        // index into the caller's request array
     int32_t q;                          // tokens of this step
-    int32_t new_from[CB_MAX_LAYERS];    // first index into the layer's free list taken by this row
+    int32_t new_from[CB_MAX_LAYERS];    // first index into the layer's free list (or the cache's allocations)
     int32_t new_count[CB_MAX_LAYERS];
+    int32_t matched;                    // prompt tokens reused from the prefix cache (whole blocks)
+    int32_t match_from;                 // first index of its matched pages in the step's list of matches
+    int32_t n_match;                    // matched blocks
 };
 
 }  // namespace
@@ -78,6 +82,7 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
         if (rq.state != CB_DECODING && rq.state != CB_PREFILLING && rq.state != CB_WAITING) return CB_E_INVAL;
         if (rq.num_computed < 0 || rq.num_pending < 1) return CB_E_INVAL;
         if (rq.state == CB_DECODING && rq.num_pending != 1) return CB_E_INVAL;
+        if (rq.n_prompt_blocks < 0 || (rq.n_prompt_blocks > 0 && !rq.prompt_hashes)) return CB_E_INVAL;
         for (int l = 0; l < L; ++l) {
             if (rq.n_pages[l] < 0 || (rq.n_pages[l] > 0 && !rq.pages[l])) return CB_E_INVAL;
             if (layers[l].ring_len > 0) {
@@ -88,6 +93,30 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
         }
     }
 
+    // Prefix sharing: only with a cache and one full-attention layer type; then the cache allocates every page.
+    cb_prefix_cache *pc = (params->prefix_cache && L == 1 && layers[0].ring_len == 0) ? params->prefix_cache : nullptr;
+    if (pc) {
+        // the scheduler will change the cache, so the output must be known to fit before anything is scheduled:
+        // check against a bound (rows, tokens and table width at their largest)
+        const int64_t n_max = std::min<int64_t>(n_reqs, cap);
+        int64_t w_max = 0;
+        for (int32_t i = 0; i < n_reqs; ++i)
+            w_max = std::max<int64_t>(w_max, ceil_div(int64_t(reqs[i].num_computed) +
+                                                      std::min(reqs[i].num_pending, budget0), P));
+        const int64_t bound = 4 * (n_max + 1) + n_reqs + n_max * w_max + budget0 + n_max;
+        if (!out || out_capacity < bound) {
+            std::memset(step, 0, sizeof(*step));
+            step->used = bound;
+            return CB_E_CAPACITY;
+        }
+    }
+    auto cache_free = [&]() -> int64_t {
+        int32_t a = 0, b = 0, c = 0;
+        cb_pcache_stats(pc, &a, &b, &c);
+        return int64_t(a) + b;
+    };
+    std::vector<int32_t> alloc;          // pages the cache allocated, in scheduling order
+    std::vector<int32_t> match_pages;    // pages matched at admission, in scheduling order
     int32_t taken[CB_MAX_LAYERS] = {0, 0};
     auto pages_needed = [&](const cb_req &rq, int32_t q, int32_t *need) {
         for (int l = 0; l < L; ++l) {
@@ -96,9 +125,10 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
             need[l] = int32_t(std::max<int64_t>(0, want - rq.n_pages[l]));
         }
     };
+    auto free_of = [&](int l) -> int64_t { return pc ? cache_free() : int64_t(layers[l].n_free) - taken[l]; };
     auto available = [&](const int32_t *need) {
         for (int l = 0; l < L; ++l)
-            if (need[l] > layers[l].n_free - taken[l]) return false;
+            if (need[l] > free_of(l)) return false;
         return true;
     };
 
@@ -108,13 +138,23 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
     int32_t held = 0;
     int32_t budget = budget0;
     auto n_rows = [&]() { return int32_t(rows[0].size() + rows[1].size() + rows[2].size()); };
-    auto schedule = [&](int32_t group, int32_t i, int32_t q, const int32_t *need) {
+    auto schedule = [&](int32_t group, int32_t i, int32_t q, const int32_t *need, int32_t n_match = 0,
+                        int32_t match_from = 0) {
         Scheduled s{};
         s.req = i;
         s.q = q;
+        s.n_match = n_match;
+        s.matched = n_match * P;
+        s.match_from = match_from;
         for (int l = 0; l < L; ++l) {
-            s.new_from[l] = taken[l];
             s.new_count[l] = need[l];
+            if (pc) {   // one layer type: the cache allocates (availability was checked)
+                s.new_from[l] = int32_t(alloc.size());
+                alloc.resize(alloc.size() + size_t(need[l]));
+                if (need[l] > 0) cb_pcache_allocate(pc, need[l], alloc.data() + s.new_from[l]);
+            } else {
+                s.new_from[l] = taken[l];
+            }
             taken[l] += need[l];
         }
         rows[group].push_back(s);
@@ -159,21 +199,42 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
             for (int l = 0; l < L; ++l) {
                 const cb_layer_pool &lay = layers[l];
                 if (lay.pool_pages > 0 &&
-                    double(lay.n_free - taken[l]) < double(params->safety_margin) * double(lay.pool_pages))
+                    double(free_of(l)) < double(params->safety_margin) * double(lay.pool_pages))
                     low = true;
             }
             if (low) {
                 held = 1;
                 break;
             }
-            const int32_t q = std::min(reqs[i].num_pending, budget);
+            const cb_req &rq = reqs[i];
+            int32_t found = 0, free_found = 0;
+            if (pc && rq.num_computed == 0 && rq.n_pages[0] == 0 && rq.n_prompt_blocks > 0) {
+                // leading cached blocks of the prompt, leaving at least one prompt token to compute
+                const int32_t n = std::min(rq.n_prompt_blocks, (rq.num_pending - 1) / P);
+                std::vector<int32_t> hit(size_t(std::max(n, 1)));
+                cb_pcache_lookup(pc, rq.prompt_hashes, n, hit.data(), &found, &free_found);
+            }
+            const int32_t q = std::min(rq.num_pending - found * P, budget);
             int32_t need[CB_MAX_LAYERS];
-            pages_needed(reqs[i], q, need);
-            if (!available(need)) {
+            bool ok;
+            if (found > 0) {
+                need[0] = int32_t(std::max<int64_t>(0, ceil_div(int64_t(found) * P + q, P) - found));
+                ok = need[0] <= free_of(0) - free_found;   // matched free pages leave the free pool
+            } else {
+                pages_needed(rq, q, need);
+                ok = available(need);
+            }
+            if (!ok) {
                 first_rejected = i;
                 break;
             }
-            schedule(2, i, q, need);
+            const int32_t match_from = int32_t(match_pages.size());
+            if (found > 0) {
+                match_pages.resize(match_pages.size() + size_t(found));
+                int32_t got = 0;
+                cb_pcache_match(pc, rq.prompt_hashes, found, match_pages.data() + match_from, &got);
+            }
+            schedule(2, i, q, need, found, match_from);
         }
     };
     if (params->policy == CB_POLICY_FIFO) {
@@ -199,7 +260,7 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
     for (const Scheduled &s : all) {
         T += s.q;
         max_q = std::max(max_q, s.q);
-        max_seq = std::max(max_seq, reqs[s.req].num_computed + s.q);
+        max_seq = std::max(max_seq, reqs[s.req].num_computed + s.matched + s.q);
     }
     if (T > INT32_MAX) return CB_E_INVAL;
     std::memset(step, 0, sizeof(*step));
@@ -211,11 +272,13 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
     step->n_stalled = int32_t(stalled.size());
     step->first_rejected = first_rejected;
     step->held_by_margin = held;
+    step->prefix_sharing = pc ? 1 : 0;
     int64_t off = 0;
     step->off_query_start_loc = off; off += N + 1;
     step->off_seq_lens = off;        off += N;
     step->off_req_index = off;       off += N;
     step->off_stalled = off;         off += int64_t(stalled.size());
+    step->off_matched = off;         off += N;
     for (int l = 0; l < L; ++l) {
         step->used_pages[l] = taken[l];
         const int32_t width = layers[l].ring_len > 0 ? layers[l].ring_len : int32_t(ceil_div(max_seq, P));
@@ -234,8 +297,9 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
     qsl[0] = 0;
     for (int32_t r = 0; r < N; ++r) {
         qsl[r + 1] = qsl[r] + all[r].q;
-        seq[r] = reqs[all[r].req].num_computed + all[r].q;
+        seq[r] = reqs[all[r].req].num_computed + all[r].matched + all[r].q;
         idx[r] = all[r].req;
+        out[step->off_matched + r] = all[r].matched;
     }
     std::copy(stalled.begin(), stalled.end(), out + step->off_stalled);
 
@@ -251,19 +315,23 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
             const Scheduled &s = all[r];
             const cb_req &rq = reqs[s.req];
             int32_t *row = table + int64_t(r) * width;
-            // the row's pages: those owned, then those just taken from the free list
+            // the row's pages: those owned, those matched in the prefix cache, then the fresh ones (from the free
+            // list, or allocated by the cache)
             const int32_t used = R > 0 ? R : int32_t(ceil_div(seq[r], P));
+            const int32_t own = rq.n_pages[l];
+            const int32_t *fresh = pc ? alloc.data() : lay.free_pages;
             for (int32_t b = 0; b < width; ++b) {
                 int32_t page = params->pad_page;
                 if (b < used) {
-                    page = b < rq.n_pages[l] ? rq.pages[l][b]
-                                             : lay.free_pages[s.new_from[l] + (b - rq.n_pages[l])];
+                    if (b < own) page = rq.pages[l][b];
+                    else if (b - own < s.n_match) page = match_pages[size_t(s.match_from + b - own)];
+                    else page = fresh[s.new_from[l] + (b - own - s.n_match)];
                 }
                 row[b] = page;
             }
             rlen[r] = R;
             for (int32_t j = 0; j < s.q; ++j)
-                slots[qsl[r] + j] = int32_t(slot_of(row, int64_t(rq.num_computed) + j, P, R));
+                slots[qsl[r] + j] = int32_t(slot_of(row, int64_t(rq.num_computed) + s.matched + j, P, R));
         }
     }
     const bool blocked = !stalled.empty() || first_rejected >= 0;

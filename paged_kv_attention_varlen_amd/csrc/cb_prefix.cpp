@@ -123,6 +123,21 @@ extern "C" cb_status cb_pcache_match(cb_prefix_cache *c, const uint64_t *hashes,
     return CB_OK;
 }
 
+extern "C" cb_status cb_pcache_lookup(const cb_prefix_cache *c, const uint64_t *hashes, int32_t n_blocks,
+                                      int32_t *pages_out, int32_t *n_found, int32_t *n_free_found) {
+    if (!c || n_blocks < 0 || (n_blocks > 0 && (!hashes || !pages_out))) return CB_E_INVAL;
+    int32_t m = 0, free_hits = 0;
+    for (; m < n_blocks; ++m) {
+        const auto it = c->index.find(hashes[m]);
+        if (it == c->index.end()) break;
+        pages_out[m] = it->second;
+        if (c->ref[size_t(it->second)] == 0) ++free_hits;
+    }
+    if (n_found) *n_found = m;
+    if (n_free_found) *n_free_found = free_hits;
+    return CB_OK;
+}
+
 extern "C" cb_status cb_pcache_allocate(cb_prefix_cache *c, int32_t n, int32_t *pages_out) {
     if (!c || n < 0 || (n > 0 && !pages_out)) return CB_E_INVAL;
     if (int64_t(c->uninit.size()) + int64_t(c->init_free.size()) < n) return CB_E_NOSPACE;

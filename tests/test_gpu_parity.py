@@ -385,29 +385,51 @@ def test_swap_out_and_back_preserves_outputs(torch_gpu):
 
 
 def test_prefix_sharing_step(torch_gpu):
-    """Two requests share the pages of a common prompt prefix through the prefix cache: A has prefilled 100 prompt
-    tokens (6 full blocks registered); B's prompt starts with the same 96 tokens, so B reuses A's first 6 pages and
-    prefills only its remaining 40 tokens, from context 96, while A decodes. The step's outputs match the oracle, and
-    B's rows are bitwise those of a run where B holds private copies of the prefix pages."""
+    """Prefix sharing at admission, end to end. Step 1 (host only): A's 100-token prompt is admitted; its six full
+    blocks are then registered in the prefix cache. Step 2: A decodes while B, whose prompt starts with A's first 96
+    tokens, is admitted: the scheduler matches A's six pages, B's context starts at 96 and it prefills only its 40
+    remaining tokens. The metadata (block table with the shared pages, slots) comes from cb_build_metadata and
+    equals the oracle scheduler's; the device step's outputs match the oracle's paged attention over the same
+    caches; and B's rows are bitwise those of a run where B holds private copies of the prefix pages."""
     import torch
     import paged_kv_attention_varlen_amd as cb
     from oracle import prefix_cache as O
+    from oracle import scheduler as OS
     from synth import round_to_bf16
     rng = np.random.default_rng(21)
     P, Hq, Hkv, D, n_pages = 16, 8, 2, 128, 64
     prompt_a = rng.integers(0, 30000, 100).astype(np.int32)
     prompt_b = np.concatenate([prompt_a[:96], rng.integers(0, 30000, 40).astype(np.int32)])
-    pc = cb.PrefixCache(n_pages, np.arange(2, n_pages, dtype=np.int32))
-    pages_a = pc.allocate(-(-101 // P))                                # A's 100 keys plus this step's token
-    for b, h in enumerate(cb.block_hashes(prompt_a, P)):
-        pc.commit(int(pages_a[b]), h)
-    hb = cb.block_hashes(prompt_b[:-1], P)                              # blocks of B's prompt
-    shared = pc.match(hb)
-    assert shared.tolist() == pages_a[:6].tolist()
-    assert hb.tolist()[:6] == O.block_hashes(prompt_b[:-1], P)[:6]
-    ctx_b = shared.size * P                                             # B skips the prefill of 96 tokens
-    pages_b = np.concatenate([shared, pc.allocate(-(-len(prompt_b) // P) - shared.size)])
-    assert pc.page_info(int(shared[0]))[0] == 2                         # both requests hold the shared page
+    free0 = np.arange(2, n_pages, dtype=np.int32)
+    pc, oc = cb.PrefixCache(n_pages, free0), O.PrefixCache(n_pages, free0.tolist())
+    pools = [{"ring_len": 0, "window_left": -1, "pool_pages": n_pages - 2, "free_pages": np.zeros(0, np.int32)}]
+    hashes = {0: O.block_hashes(prompt_a, P), 1: O.block_hashes(prompt_b, P)}
+    assert cb.block_hashes(prompt_b, P).tolist() == hashes[1]
+
+    def schedule(reqs):
+        hs = [hashes[r.id] for r in reqs]
+        got = cb.build_metadata(reqs, pools, 512, 8, P, 0.0, 0, prefix_cache=pc, prompt_hashes=hs)
+        want = OS.build_metadata(reqs, pools, 512, 8, P, 0.0, 0, prefix_cache=oc, prompt_hashes=hs)
+        for key in ("query_start_loc", "seq_lens", "matched_tokens"):
+            assert np.array_equal(got[key], want[key]), key
+        for key in ("block_table", "slot_mapping"):
+            assert np.array_equal(got["layers"][0][key], want["layers"][0][key]), key
+        return got, hs
+
+    reqs = [cb.Request(0, WAITING, 0, 100, [np.zeros(0, np.int32)])]
+    s1, hs = schedule(reqs)
+    reqs, _ = cb.advance(reqs, s1, [np.zeros(0, np.int32)], [0], P, pc, hs)
+    cb.advance([cb.Request(0, WAITING, 0, 100, [np.zeros(0, np.int32)])], s1, [np.zeros(0, np.int32)], [0], P, oc,
+               hs)
+    pages_a = reqs[0].pages[0]
+    assert pc.stats()[2] == 6                                            # A's six full blocks are registered
+    reqs.append(cb.Request(1, WAITING, 0, len(prompt_b), [np.zeros(0, np.int32)]))
+    s2, _ = schedule(reqs)
+    qsl, seq = s2["query_start_loc"], s2["seq_lens"]
+    table, slots = s2["layers"][0]["block_table"], s2["layers"][0]["slot_mapping"]
+    assert s2["matched_tokens"].tolist() == [0, 96] and seq.tolist() == [101, 136]
+    assert table[1, :6].tolist() == pages_a[:6].tolist()                 # B's first six pages are A's
+    assert pc.page_info(int(pages_a[0]))[0] == 2
 
     # caches: A's history (100 keys) on its pages; B's context is A's (same tokens, same pages)
     kc = np.full((n_pages, P, Hkv, D), np.nan, np.float32)
@@ -417,23 +439,14 @@ def test_prefix_sharing_step(torch_gpu):
     for pos in range(100):
         kc[pages_a[pos // P], pos % P] = hist_k[pos]
         vc[pages_a[pos // P], pos % P] = hist_v[pos]
-    # the step: A decodes 1 token at position 100, B prefills 40 at positions 96..135
-    qsl = np.array([0, 1, 41], np.int32)
-    seq = np.array([101, ctx_b + 40], np.int32)
-    width = max(pages_a.size, pages_b.size)
-    table = np.zeros((2, width), np.int32)
-    table[0, :pages_a.size], table[1, :pages_b.size] = pages_a, pages_b
-    new_k = round_to_bf16(rng.standard_normal((41, Hkv, D)).astype(np.float32))
-    new_v = round_to_bf16(rng.standard_normal((41, Hkv, D)).astype(np.float32))
-    q = round_to_bf16(rng.standard_normal((41, Hq, D)).astype(np.float32))
-    pos_of = [100] + list(range(ctx_b, ctx_b + 40))
-    rows_of = [0] + [1] * 40
-    slots = np.array([table[r][p // P] * P + p % P for r, p in zip(rows_of, pos_of)], np.int32)
+    T = int(qsl[-1])
+    new_k = round_to_bf16(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    new_v = round_to_bf16(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    q = round_to_bf16(rng.standard_normal((T, Hq, D)).astype(np.float32))
 
-    def run(tab, kcache, vcache):
+    def run(tab, sl, kcache, vcache):
         kd = torch.from_numpy(kcache.transpose(0, 2, 1, 3).copy()).to(torch.bfloat16).cuda()
         vd = torch.from_numpy(vcache.transpose(0, 2, 3, 1).copy()).to(torch.bfloat16).cuda()
-        sl = np.array([tab[r][p // P] * P + p % P for r, p in zip(rows_of, pos_of)], np.int32)
         cb.kv_append(kd, vd, torch.from_numpy(new_k).to(torch.bfloat16).cuda(),
                      torch.from_numpy(new_v).to(torch.bfloat16).cuda(), torch.from_numpy(sl).cuda())
         qd = torch.from_numpy(q).to(torch.bfloat16).cuda()
@@ -445,20 +458,19 @@ def test_prefix_sharing_step(torch_gpu):
         torch.cuda.synchronize()
         return out
 
-    got = run(table, kc, vc)
-    # oracle: the append, then attention through the shared block table
+    got = run(table, slots, kc, vc)
     ko, vo = kc.copy(), vc.copy()
     A.kv_append(ko, vo, new_k, new_v, slots, P)
     ref = A.paged_attention(q, ko.astype(np.float64), vo.astype(np.float64), qsl, seq, table, P, 1 / np.sqrt(D))
     err = np.abs(got.float().cpu().numpy() - ref)
     assert err.max() <= H.TOL_BF16_MAX and err.mean() <= H.TOL_BF16_MEAN
-    # without sharing: B's prefix copied to private pages 40.. ; B's rows are bitwise the same
+    # without sharing: B's prefix copied to private pages; B's rows are bitwise the same
+    spare = [p for p in range(2, n_pages) if p not in set(table.reshape(-1).tolist())][:6]
     private = table.copy()
-    private[1, :6] = np.arange(40, 46)
+    private[1, :6] = spare
     kp, vp = kc.copy(), vc.copy()
-    kp[40:46], vp[40:46] = kc[pages_a[:6]], vc[pages_a[:6]]
-    alone = run(private, kp, vp)
+    kp[spare], vp[spare] = kc[pages_a[:6]], vc[pages_a[:6]]
+    sl_private = np.array([private[r][p // P] * P + p % P for r, p in
+                           [(0, 100)] + [(1, x) for x in range(96, 136)]], np.int32)
+    alone = run(private, sl_private, kp, vp)
     assert torch.equal(got[1:], alone[1:])
-    pc.release(pages_a)
-    pc.release(pages_b)
-    assert pc.stats()[1] == 6                                            # A's registered blocks stay initialized

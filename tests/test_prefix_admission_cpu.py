@@ -109,3 +109,68 @@ def test_a_ring_layer_turns_sharing_off():
     assert not s["prefix_sharing"] and s["matched_tokens"].tolist() == [0]
     assert s["layers"][0]["block_table"].tolist() == [[30, 31, 32, 33]]
     assert (list(cache.ref), cache.stats()) == before
+
+
+def _cache_state(c, n_pages, lib_side):
+    if lib_side:
+        info = [c.page_info(p) for p in range(n_pages)]
+        return c.stats(), [(r, bool(reg), h if reg else 0) for r, reg, h in info]
+    return c.stats(), [(c.ref[p], c.hash[p] is not None, c.hash[p] or 0) for p in range(n_pages)]
+
+
+import pytest  # noqa: E402
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_library_matches_oracle_on_random_shared_prefix_loops(seed):
+    """Random serving loops with shared prompt prefixes: requests arrive, share prefixes of a few base prompts,
+    prefill in chunks, decode and finish (releasing their pages). Every step the library's schedule equals the
+    oracle's (metadata, matched context, pages) and both caches hold the same state; the same lifecycle then moves
+    both request lists on, registering the prompt blocks each step completed."""
+    import paged_kv_attention_varlen_amd as cb
+    rng = np.random.default_rng(seed)
+    P = int(rng.choice([4, 8, 16]))
+    n_pages = int(rng.integers(40, 120))
+    free0 = rng.permutation(np.arange(2, n_pages)).astype(np.int32)
+    cc, co = cb.PrefixCache(n_pages, free0), O.PrefixCache(n_pages, free0.tolist())
+    bases = [rng.integers(0, 1000, 6 * P).astype(np.int32) for _ in range(3)]
+    prompts, reqs_c, reqs_o = {}, [], []
+    next_id = 0
+    budget = int(rng.integers(P, 6 * P))
+    pools = [{"ring_len": 0, "window_left": -1, "pool_pages": n_pages - 2, "free_pages": np.zeros(0, np.int32)}]
+    matched_any = False
+    for step in range(14):
+        for _ in range(int(rng.integers(0, 3))):            # arrivals
+            b = bases[int(rng.integers(0, 3))]
+            head = b[:int(rng.integers(0, len(b) + 1))]
+            prompt = np.concatenate([head, rng.integers(0, 1000, int(rng.integers(1, 3 * P)))]).astype(np.int32)
+            prompts[next_id] = prompt
+            for lst in (reqs_c, reqs_o):
+                lst.append(cb.Request(next_id, WAIT, 0, len(prompt), [np.zeros(0, np.int32)]))
+            next_id += 1
+        hashes = [O.block_hashes(prompts[r.id], P) for r in reqs_c]
+        sc = cb.build_metadata(reqs_c, pools, budget, 8, P, 0.1, 0, prefix_cache=cc, prompt_hashes=hashes)
+        so = S.build_metadata(reqs_o, pools, budget, 8, P, 0.1, 0, prefix_cache=co, prompt_hashes=hashes)
+        assert (sc["status"] == 0) == (so["status"] == "ok") or (sc["status"] == 2 and so["status"] == "nospace")
+        if so["status"] == "inval":
+            break
+        for key in ("query_start_loc", "seq_lens", "req_index", "matched_tokens", "stalled"):
+            assert np.array_equal(sc[key], so[key]), (seed, step, key)
+        assert sc["first_rejected"] == so["first_rejected"] and sc["held_by_margin"] == so["held_by_margin"]
+        for key in ("block_table", "slot_mapping"):
+            assert np.array_equal(sc["layers"][0][key], so["layers"][0][key]), (seed, step, key)
+        assert sc["layers"][0]["used_pages"] == so["layers"][0]["used_pages"]
+        matched_any |= bool(np.any(so["matched_tokens"] > 0))
+        reqs_c, _ = cb.advance(reqs_c, sc, [np.zeros(0, np.int32)], [0], P, cc, hashes)
+        reqs_o, _ = cb.advance(reqs_o, so, [np.zeros(0, np.int32)], [0], P, co, hashes)
+        assert _cache_state(cc, n_pages, True) == _cache_state(co, n_pages, False), (seed, step)
+        # a decoding request finishes now and then: its pages go back (shared ones stay with their other holders)
+        done = [k for k, r in enumerate(reqs_c) if r.state == DEC and rng.random() < 0.3]
+        for k in sorted(done, reverse=True):
+            pages = reqs_c[k].pages[0]
+            cc.release(pages)
+            assert co.release([int(p) for p in pages])
+            del reqs_c[k], reqs_o[k]
+        assert _cache_state(cc, n_pages, True) == _cache_state(co, n_pages, False), (seed, step, "release")
+    assert next_id > 0
+    assert matched_any, "the random loop never shared a prefix"
