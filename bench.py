@@ -16,8 +16,9 @@ steps between two device synchronisations: `value` is query tokens per second ov
 Per-kernel durations come from fence-free HIP events recorded on the compute stream around the decode, prefill and
 merge launches of every EVENTS_EVERY-th timed step. A second pass of steps, each bracketed by step-boundary events,
 gives the p10/p50/p90 step times; a third runs steps after a 1 GiB write (larger than the 256 MB last-level cache)
-and reports the kernels' rooflines without a warm cache. The mixed 2048-token step, the decode-only step and the
-large decode batch are measured the same way and reported under `per_config`.
+and reports the kernels' rooflines without a warm cache; a fourth times the same step with the prefill kernels on a
+second stream beside the decode kernel (only its step time: the kernels then share the GPU). The mixed 2048-token
+step, the decode-only step and the large decode batch are measured the same way and reported under `per_config`.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -240,7 +241,8 @@ def _rooflines(w, step, work, fused, dec_us, pre_us, n_sampled):
     return roofline, roofline_prefill
 
 
-def measure(index: int, steps: int, warmup: int, args, dist_steps: int, flush_steps: int = 0):
+def measure(index: int, steps: int, warmup: int, args, dist_steps: int, flush_steps: int = 0,
+            concurrent_steps: int = 0):
     """Set up a workload and time it (see the module docstring). Returns (result dict, workload, step, schedule)."""
     import torch
     from harness import build_step, pipeline_for
@@ -334,6 +336,25 @@ def measure(index: int, steps: int, warmup: int, args, dist_steps: int, flush_st
                           "prefill_us": frp["avg_launch_us"] if frp else None}
     if args.graphs:
         res["graphs"] = {"captured": pipe.captures, "replayed": pipe.replays}
+    if concurrent_steps and not args.concurrent:
+        # the same step with the prefill-tile kernels on a second stream beside the decode kernel (the append then
+        # runs as a launch of its own first, since the concurrent prefill kernels read the appended keys): the two
+        # kernels share the GPU, so only the step time is reported
+        cp = pipeline_for(w, step, decode_split=args.decode_split, prefill_split=args.prefill_split,
+                          concurrent=True, copy_stream=not args.no_copy_stream)
+        for _ in range(warmup):
+            cp.run()
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        for _ in range(concurrent_steps):
+            cp.run()
+        torch.cuda.synchronize()
+        cms = (time.perf_counter() - c0) * 1e3 / concurrent_steps
+        res["concurrent_prefill_stream"] = {"steps": concurrent_steps, "warmup": warmup,
+                                            "ms_per_step": round(cms, 5), "value": round(T / (cms / 1e3), 1),
+                                            "unit": "query tokens/s"}
+        log(f"[bench] workload {index}: concurrent prefill stream {cms:.4f} ms/step")
+        del cp
     return res, w, step, pipe
 
 
@@ -351,6 +372,9 @@ def main():
     ap.add_argument("--dist-steps", type=int, default=40, help="steps of the step-time distribution pass")
     ap.add_argument("--flush-steps", type=int, default=10,
                     help="steps of the headline run after a 1 GiB write each (0: skip)")
+    ap.add_argument("--concurrent-steps", type=int, default=20,
+                    help="steps of an extra headline pass with the prefill kernels on a second stream beside the "
+                         "decode kernel (0: skip); only its step time is reported")
     ap.add_argument("--decode-split", type=int, default=0)
     ap.add_argument("--prefill-split", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -400,7 +424,8 @@ def main():
                     "gb_per_s": round(2 * n * 4 / (ms / 1e3) / 1e9, 1)}
         del src, dst
 
-    head, w, step, pipe = measure(args.workload, args.steps, args.warmup, args, args.dist_steps, args.flush_steps)
+    head, w, step, pipe = measure(args.workload, args.steps, args.warmup, args, args.dist_steps, args.flush_steps,
+                                  args.concurrent_steps)
     sched = step.sched
     swap = measure_swap(step, args.swap_pages) if args.swap_pages else None
     del pipe, step
@@ -429,7 +454,8 @@ def main():
                    "kv_tokens_visible": head["kv_tokens_visible"]},
         "step_us": head["step_us"], "kv_gb_per_s": head["kv_gb_per_s"], "kernel_us": head["kernel_us"],
         "roofline": head["roofline"], "roofline_prefill": head["roofline_prefill"],
-        "flushed": head.get("flushed"), "per_config": per_config, "cpu_baseline": base,
+        "flushed": head.get("flushed"), "concurrent_prefill_stream": head.get("concurrent_prefill_stream"),
+        "per_config": per_config, "cpu_baseline": base,
     }
     if "graphs" in head:
         line["graphs"] = head["graphs"]
