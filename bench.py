@@ -252,8 +252,10 @@ def measure(index: int, steps: int, warmup: int, args, dist_steps: int, flush_st
     w = make_workload(index)
     log(f"[bench] workload {index}: {w.name}")
     t = time.time()
-    step = build_step(w, decode_split=args.decode_split, prefill_split=args.prefill_split, threads=16)
+    step = build_step(w, decode_split=args.decode_split, prefill_split=args.prefill_split, threads=16,
+                      prefill_rows=args.prefill_rows)
     pipe = pipeline_for(w, step, decode_split=args.decode_split, prefill_split=args.prefill_split,
+                        prefill_rows=args.prefill_rows,
                         concurrent=args.concurrent, copy_stream=not args.no_copy_stream, graphs=args.graphs)
     sched = step.sched
     log(f"[bench] setup {time.time() - t:.1f}s; N={sched['num_reqs']} T={sched['num_tokens']} "
@@ -341,6 +343,7 @@ def measure(index: int, steps: int, warmup: int, args, dist_steps: int, flush_st
         # runs as a launch of its own first, since the concurrent prefill kernels read the appended keys): the two
         # kernels share the GPU, so only the step time is reported
         cp = pipeline_for(w, step, decode_split=args.decode_split, prefill_split=args.prefill_split,
+                          prefill_rows=args.prefill_rows,
                           concurrent=True, copy_stream=not args.no_copy_stream)
         for _ in range(warmup):
             cp.run()
@@ -377,6 +380,8 @@ def main():
                          "decode kernel (0: skip); only its step time is reported")
     ap.add_argument("--decode-split", type=int, default=0)
     ap.add_argument("--prefill-split", type=int, default=0)
+    ap.add_argument("--prefill-rows", type=int, default=0, choices=(0, 128, 256),
+                    help="query rows per prefill work group (0: the planner's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--concurrent", action="store_true",

@@ -108,7 +108,7 @@ def fill_history(w, l: int, kc, vc, pool, device, dt, chunk_tokens: int = 1 << 1
 
 
 def build_step(w, device: str = "cuda", decode_split: int = 0, prefill_split: int = 0, threads: int = 8,
-               verbose: bool = False, rows: int = 0, workspace_bytes: int = 0) -> Step:
+               verbose: bool = False, rows: int = 0, workspace_bytes: int = 0, prefill_rows: int = 0) -> Step:
     """Schedule the workload's step (cb_build_metadata), plan every layer (cb_plan_attention), copy the metadata and
     plans to the device in one packed int32 buffer, and build the caches (NaN, then the history) and the step's
     new rows. rows: token capacity of the Q/K/V/output tensors (at least the step's tokens; extra rows are NaN);
@@ -130,7 +130,8 @@ def build_step(w, device: str = "cuda", decode_split: int = 0, prefill_split: in
     for l, lay in enumerate(w.layers):
         L = sched["layers"][l]
         ring = L["ring_len"] if lay.ring_len > 0 else None
-        plan = cb.plan_attention(qsl, seq, ring, Hq, Hkv, D, P, dt, lay.window_left, decode_split, prefill_split)
+        plan = cb.plan_attention(qsl, seq, ring, Hq, Hkv, D, P, dt, lay.window_left, decode_split, prefill_split,
+                                 prefill_rows)
         plans.append(plan)
         parts += [L["block_table"].reshape(-1), L["slot_mapping"], plan.buffer]
     offs = np.cumsum([0] + [p.size for p in parts])

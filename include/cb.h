@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 5
+#define CB_ABI_VERSION 6
 
 typedef int32_t cb_status;
 #define CB_OK 0
@@ -215,6 +215,11 @@ typedef struct cb_attn_shape {
                                   may change with the batch (the values stay within rounding of each other)    */
     int32_t prefill_split;     /* keys per prefill-tile split (a multiple of 64), 0 = chosen by the planner
                                   (batch-dependent in the same way as decode_split)                            */
+    int32_t prefill_rows;      /* query rows (tokens x grouped heads) per prefill work group: 128 (4 waves, two
+                                  work groups per CU), 256 (8 waves sharing each K/V tile, one per CU) or 0 =
+                                  chosen by the planner (256 when the step has enough such tiles to fill the
+                                  CUs several times over). Any other value is CB_E_INVAL. The rows of a tile see
+                                  the same keys either way; outputs agree to rounding                          */
 } cb_attn_shape;
 
 /* Header of the packed int32 plan. Work items (8 int32 each) and merge items (4 int32 each) start at the given

@@ -316,15 +316,17 @@ def _dtype_code(dtype) -> int:
 
 def plan_attention(query_start_loc, seq_lens, ring_len, num_q_heads: int, num_kv_heads: int, head_dim: int,
                    page_size: int, dtype, window_left: int = -1, decode_split: int = 0,
-                   prefill_split: int = 0) -> AttnPlan:
-    """Split a step into kernel work items (cb_plan_attention). ring_len: per-row ring lengths or None."""
+                   prefill_split: int = 0, prefill_rows: int = 0) -> AttnPlan:
+    """Split a step into kernel work items (cb_plan_attention). ring_len: per-row ring lengths or None.
+    prefill_rows: query rows per prefill work group, 128 or 256, or 0 for the planner's choice."""
     lib = _abi.load()
     qsl = _i32(query_start_loc)
     seq = _i32(seq_lens)
     n = seq.size
     rl = None if ring_len is None else _i32(ring_len)
     shape = _abi.cb_attn_shape(int(num_q_heads), int(num_kv_heads), int(head_dim), int(page_size),
-                               _dtype_code(dtype), int(window_left), int(decode_split), int(prefill_split))
+                               _dtype_code(dtype), int(window_left), int(decode_split), int(prefill_split),
+                               int(prefill_rows))
     info = _abi.cb_plan()
     cap = 1024
     while True:

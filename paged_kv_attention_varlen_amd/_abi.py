@@ -13,7 +13,7 @@ CB_DECODING, CB_PREFILLING, CB_WAITING = 0, 1, 2
 CB_MAX_LAYERS = 2
 CB_PHASE_DECODE, CB_PHASE_ROWWISE, CB_PHASE_PREFILL, CB_PHASE_COMBINE = 1, 2, 4, 8
 CB_POLICY_FIFO, CB_POLICY_PREFILL_FIRST = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 CB_LAYOUT_PAGED_NHD, CB_LAYOUT_KD_VT = 0, 1
 CB_NOALLOC_WORKSPACE_BYTES = 96 << 20
 
@@ -51,7 +51,7 @@ class cb_step(C.Structure):
 class cb_attn_shape(C.Structure):
     _fields_ = [("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("page_size", C.c_int32), ("dtype", C.c_int32), ("window_left", C.c_int32),
-                ("decode_split", C.c_int32), ("prefill_split", C.c_int32)]
+                ("decode_split", C.c_int32), ("prefill_split", C.c_int32), ("prefill_rows", C.c_int32)]
 
 
 class cb_plan(C.Structure):

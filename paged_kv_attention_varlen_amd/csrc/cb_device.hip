@@ -591,9 +591,11 @@ __global__ __launch_bounds__(64) void rowwise_kernel(const T *__restrict__ q, T 
 
 // ======================================================================= prefill tiles (bf16, MFMA 32x32x16)
 //
-// Work group = one (tile of query tokens x the G heads of a kv head = 128 rows, KV range, kv head); rows are
-// token-major (row = token * G + head) and each of the 4 waves owns 32 of them. Two work groups share a CU (two waves
-// per SIMD), so one's softmax arithmetic runs beside the other's matrix work. Per 64-key tile and wave:
+// Work group = one (tile of query tokens x the G heads of a kv head = 32 NW rows, KV range, kv head); rows are
+// token-major (row = token * G + head) and each of the NW waves owns 32 of them. Every SIMD runs two waves: two
+// 4-wave work groups share a CU (128-row tiles), or one 8-wave work group has it alone (256-row tiles, where each K/V
+// tile copied into LDS serves twice the rows). Either way one wave's softmax arithmetic runs beside the other's
+// matrix work. Per 64-key tile and wave:
 //   S^T[key][row] = K[key][:] . Q[row][:]         A = K rows (LDS), B = Q^T (registers)   2 halves x D/16 MFMAs
 //   O^T[d][row]  += V^T[d][key] . P^T[key][row]   A = V^T (LDS), B = P^T (registers)      4 k-steps x D/32 MFMAs
 // MFMA 32x32x16 bf16 operands: lane l holds A[l%32][8(l/32) .. +8] and B[8(l/32) .. +8][l%32]; the result gives lane l
@@ -607,7 +609,8 @@ __global__ __launch_bounds__(64) void rowwise_kernel(const T *__restrict__ q, T 
 // scalar; with 8-key pages a copy spans two):
 //   K block (half s, k-step pair p, key quarter qq): slot 32 kbp + 16 h + j = K[32s + 16qq + j][16(2p + kbp) + 8h ..]
 //   V block (k-step kk, d block b):                 slot 32 h + i          = V^T[32b + i][16kk + 8h ..]
-// Wave w copies key quarter w (keys 16w .. 16w + 15 of the tile: its K blocks and V k-step w).
+// Key quarter qq (keys 16qq .. 16qq + 15 of the tile: its K blocks and V k-step qq) is copied by wave qq, or with 8
+// waves by waves qq and qq + 4, each taking half of the quarter's blocks.
 //
 // Per tile, with the next tile's copies in flight (double buffering):
 //   QK(half 0) | QK(half 1) beside softmax(half 0) | PV(half 0) beside softmax(half 1) | PV(half 1)
@@ -615,7 +618,6 @@ __global__ __launch_bounds__(64) void rowwise_kernel(const T *__restrict__ q, T 
 // current maximum, and only when some row's weights could exceed 2^8 (its sum does) does a rare path move
 // it, rescale that row's accumulators and recompute the weights. Tiles every row sees completely skip the mask.
 
-constexpr int kPfRows = 128;   // query rows of one work group: 4 waves x 32
 constexpr int kPfKeys = 64;    // keys per tile
 constexpr int kPrefillMaxPages = 1536;   // page ids of one prefill item staged in LDS (split / page + 2)
 // the running maximum may lag 8 (log2 units) behind the true one: a half's weight sum above 2^8 sends the row to the
@@ -648,8 +650,8 @@ __device__ __forceinline__ float max_xor32(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int D, int PL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
+template <int D, int PL, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     const uint16_t *__restrict__ q, uint16_t *__restrict__ out, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ block_table, int table_width, int num_pages,
     const int32_t *__restrict__ items, int n_items, float *__restrict__ part_o, float *__restrict__ part_ml, int Hq,
@@ -657,7 +659,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int P = 1 << PL;
     constexpr int KB = D / 16;          // k-steps of the QK product
     constexpr int DB = D / 32;          // 32-row d blocks of the output
-    constexpr int NK = KB / 2;          // K blocks per key quarter (copies per wave per tile)
+    constexpr int NK = KB / 2;          // K blocks per key quarter
+    constexpr int KQ = NW / 4;          // waves sharing the copies of one key quarter
+    constexpr int NT = NW * 64;         // threads
+    static_assert((NW == 4 || NW == 8) && NK % KQ == 0 && DB % KQ == 0, "copies must split evenly over the waves");
     constexpr int KT = 2 * KB * 1024;   // one K tile (64 keys)
     constexpr int VT = 4 * DB * 1024;   // one V tile (64 keys)
     // distinct LDS objects per buffer: the copies streaming into one provably do not alias reads of the other, so
@@ -719,17 +724,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // ---- the item's page ids into LDS
         const int blk0 = ulo >> PL;
         const int nblk = ((uhi - 1) >> PL) - blk0 + 1;
-        for (int i = tid; i < nblk; i += 256) s_pages[i] = lookup_page(bt, blk0 + i, ring, num_pages);
+        for (int i = tid; i < nblk; i += NT) s_pages[i] = lookup_page(bt, blk0 + i, ring, num_pages);
         // keys outside the item's blocks read the nearest staged page: a real page of the pool, so the copy stays in
         // bounds; those keys are masked (K) or zeroed (V) before use
         auto page_at = [&](int key) { return s_pages[min(max((key >> PL) - blk0, 0), nblk - 1)]; };
 
-        // ---- copies of one tile into LDS: wave w copies key quarter w
+        // ---- copies of one tile into LDS: wave w copies its part (w / 4) of key quarter w % 4
+        const int qw = w & 3, part = w >> 2;
         const int k_cp = (lane & (P >= 16 ? 15 : 7)) * D + 16 * (lane >> 5) + 8 * ((lane >> 4) & 1);
         const int v_cp = (lane & 31) * P + (P >= 16 ? 8 * (lane >> 5) : 0);
         auto issue_k = [&](int tile, uint8_t *kbuf) {
-            const int key0 = tile * kPfKeys + 16 * w;
-            uint8_t *dst = kbuf + ((w >> 1) * NK * 2 + (w & 1)) * 1024;
+            const int key0 = tile * kPfKeys + 16 * qw;
+            uint8_t *dst = kbuf + ((qw >> 1) * NK * 2 + (qw & 1)) * 1024;
             const uint16_t *src;
             if constexpr (P >= 16) {
                 const int pg = __builtin_amdgcn_readfirstlane(page_at(key0));
@@ -739,11 +745,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 src = kc_g + int64_t(pg) * page_elems + k_cp;
             }
 #pragma unroll
-            for (int p = 0; p < NK; ++p) load_lds16(src + 32 * p, dst + p * 2048);
+            for (int i = 0; i < NK / KQ; ++i) {
+                const int p = part * (NK / KQ) + i;
+                load_lds16(src + 32 * p, dst + p * 2048);
+            }
         };
         auto issue_v = [&](int tile, uint8_t *vbuf) {
-            const int key0 = tile * kPfKeys + 16 * w;
-            uint8_t *dst = vbuf + w * DB * 1024;
+            const int key0 = tile * kPfKeys + 16 * qw;
+            uint8_t *dst = vbuf + qw * DB * 1024;
             const uint16_t *src;
             if constexpr (P >= 16) {
                 const int pg = __builtin_amdgcn_readfirstlane(page_at(key0));
@@ -753,11 +762,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 src = vc_g + int64_t(pg) * page_elems + v_cp;
             }
 #pragma unroll
-            for (int b = 0; b < DB; ++b) load_lds16(src + 32 * b * P, dst + b * 1024);
+            for (int i = 0; i < DB / KQ; ++i) {
+                const int b = part * (DB / KQ) + i;
+                load_lds16(src + 32 * b * P, dst + b * 1024);
+            }
         };
         // zero V^T entries of keys outside [ulo, uhi) (their pages may hold anything, NaN included)
         auto fix_v = [&](int tile, uint8_t *vbuf) {
-            for (int e = tid; e < 4 * DB * 64; e += 256) {
+            for (int e = tid; e < 4 * DB * 64; e += NT) {
                 const int key8 = tile * kPfKeys + 16 * ((e >> 6) / DB) + 8 * ((e >> 5) & 1);
                 if (key8 >= ulo && key8 + 8 <= uhi) continue;
                 u32x4 *p = reinterpret_cast<u32x4 *>(vbuf + e * 16);
@@ -1095,7 +1107,9 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
     const bool bf16 = sh.dtype == CB_DTYPE_BF16;
     if ((pl.n_decode > 0 || pl.n_prefill > 0) && (!bf16 || sh.page_size < 8)) return CB_E_INVAL;
     if (pl.n_decode > 0 && (G > 16 || pl.decode_split / sh.page_size + 2 > kDecodeMaxPages)) return CB_E_INVAL;
-    if (pl.n_prefill > 0 && (G > kPfRows || kPfRows % G != 0 || pl.prefill_tokens != kPfRows / G ||
+    // prefill tiles: prefill_tokens tokens x G heads = 128 rows (4-wave work groups) or 256 (8 waves)
+    const int64_t pf_rows = int64_t(pl.prefill_tokens) * G;
+    if (pl.n_prefill > 0 && (pl.prefill_tokens < 1 || (pf_rows != 128 && pf_rows != 256) ||
                              pl.prefill_split / sh.page_size + 2 > kPrefillMaxPages))
         return CB_E_INVAL;
     const size_t need = cb_paged_attention_workspace_size(a);
@@ -1168,10 +1182,16 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
         uint16_t *oo = static_cast<uint16_t *>(a->out);
         const uint16_t *kk = static_cast<const uint16_t *>(a->k_cache);
         const uint16_t *vv = static_cast<const uint16_t *>(a->v_cache);
+        const bool wide = pf_rows == 256;   // 8-wave work groups
 #define CB_PREFILL(DD, PLOG)                                                                                   \
-    hipLaunchKernelGGL((prefill_kernel<DD, PLOG>), grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,      \
-                       a->table_width, a->num_pages, plan + pl.off_prefill, pl.n_prefill, part_o, part_ml, Hq, \
-                       Hkv, sl2e, sh.window_left, a->counts)
+    if (wide)                                                                                                  \
+        hipLaunchKernelGGL((prefill_kernel<DD, PLOG, 8>), grid, dim3(512), 0, s, qq, oo, kk, vv, a->block_table, \
+                           a->table_width, a->num_pages, plan + pl.off_prefill, pl.n_prefill, part_o, part_ml, Hq, \
+                           Hkv, sl2e, sh.window_left, a->counts);                                            \
+    else                                                                                                       \
+        hipLaunchKernelGGL((prefill_kernel<DD, PLOG, 4>), grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table, \
+                           a->table_width, a->num_pages, plan + pl.off_prefill, pl.n_prefill, part_o, part_ml, Hq, \
+                           Hkv, sl2e, sh.window_left, a->counts)
 #define CB_PREFILL_D(DD)                                                                                       \
     switch (Pl) {                                                                                              \
         case 3: CB_PREFILL(DD, 3); break;                                                                      \

@@ -398,7 +398,8 @@ extern "C" cb_status cb_validate_metadata(const int32_t *qsl, const int32_t *seq
 
 namespace {
 
-constexpr int kPrefillRows = 128;       // query rows (token x grouped head) of one prefill tile
+constexpr int kPrefillRowsNarrow = 128;  // query rows (token x grouped head) of a 4-wave prefill work group
+constexpr int kPrefillRowsWide = 256;    // ... of an 8-wave one
 constexpr int kPrefillMaxPages = 1536;  // page ids of one prefill item the device kernel stages in LDS
 constexpr int kNumCUs = 256;
 
@@ -416,6 +417,8 @@ extern "C" cb_status cb_plan_attention(const int32_t *qsl, const int32_t *seq_le
     if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || sh->window_left < -1) return CB_E_INVAL;
     if (sh->decode_split < 0 || sh->decode_split % 64 != 0) return CB_E_INVAL;
     if (sh->prefill_split < 0 || sh->prefill_split % 64 != 0) return CB_E_INVAL;
+    if (sh->prefill_rows != 0 && sh->prefill_rows != kPrefillRowsNarrow && sh->prefill_rows != kPrefillRowsWide)
+        return CB_E_INVAL;
     if ((D != 64 && D != 128) || !is_pow2(P) || P > 256) return CB_E_UNSUPPORTED;
     if (sh->dtype != CB_DTYPE_F32 && sh->dtype != CB_DTYPE_BF16) return CB_E_UNSUPPORTED;
     if (N > 0 && qsl[0] != 0) return CB_E_INVAL;
@@ -428,9 +431,24 @@ extern "C" cb_status cb_plan_attention(const int32_t *qsl, const int32_t *seq_le
     const int32_t W = sh->window_left;
     const bool bf16 = sh->dtype == CB_DTYPE_BF16;
     const bool fast_decode = bf16 && P >= 8 && G <= 16;
-    const bool fast_prefill = bf16 && P >= 8 && G <= kPrefillRows && kPrefillRows % G == 0;
-    const int32_t tile_tokens = fast_prefill ? kPrefillRows / G : 0;
     auto lo_of = [&](int64_t pos) -> int64_t { return W < 0 ? 0 : std::max<int64_t>(0, pos - W); };
+    // Prefill tile rows. 256-row tiles (8 waves) copy each K/V tile into LDS once for twice the rows of a 128-row
+    // tile, but give half as many work groups and run one per CU: chosen when the step's chunks fill the CUs with
+    // at least three of them each.
+    int32_t rows = sh->prefill_rows;
+    if (rows == 0) {
+        rows = kPrefillRowsNarrow;
+        if (bf16 && P >= 8 && kPrefillRowsWide % G == 0) {
+            int64_t wide_tiles = 0;
+            for (int32_t r = 0; r < N; ++r) {
+                const int32_t q = qsl[r + 1] - qsl[r];
+                if (q > 1) wide_tiles += ceil_div(q, kPrefillRowsWide / G);
+            }
+            if (wide_tiles * Hkv >= 3 * kNumCUs) rows = kPrefillRowsWide;
+        }
+    }
+    const bool fast_prefill = bf16 && P >= 8 && G <= rows && rows % G == 0;
+    const int32_t tile_tokens = fast_prefill ? rows / G : 0;
 
     // ---- split sizes. Decode: enough (row, split, kv head) work groups to give every CU several; prefill: tiles
     // with long key ranges are cut so that no work group carries many times the average work.
@@ -457,8 +475,9 @@ extern "C" cb_status cb_plan_attention(const int32_t *qsl, const int32_t *seq_le
     int32_t PS = sh->prefill_split;
     if (PS == 0) {
         // Split a tile's key range only as far as load balance needs: every split writes fp32 partial rows that the
-        // merge reads back. Items may be up to ~1.25x the average work of one of the ~2 work-group slots per CU.
-        const int64_t slots = 2 * kNumCUs;
+        // merge reads back. Items may be up to ~1.25x the average work of one work-group slot (two per CU with
+        // 128-row tiles, one with 256-row tiles).
+        const int64_t slots = (rows == kPrefillRowsWide ? 1 : 2) * kNumCUs;
         const int64_t per_slot = ceil_div(tile_work * Hkv, slots);
         PS = int32_t(std::min<int64_t>(1 << 20, std::max<int64_t>(512, ceil_div(per_slot * 5 / 4, 64) * 64)));
     }

@@ -122,7 +122,7 @@ class StepPipeline:
     """
 
     def __init__(self, step: Step, scheduler: Scheduler, decode_split: int = 0, prefill_split: int = 0,
-                 concurrent: bool = False, copy_stream: bool = True, graphs: bool = False, fused_append: bool = True,
+                 prefill_rows: int = 0, concurrent: bool = False, copy_stream: bool = True, graphs: bool = False, fused_append: bool = True,
                  q_interval: int = 64, kv_interval: int = 256, item_interval: int = 64, max_graphs: int = 8):
         torch = _torch()
         self.step = step
@@ -136,7 +136,7 @@ class StepPipeline:
         dt = _abi.CB_DTYPE_BF16 if str(step.dtype) == "torch.bfloat16" else _abi.CB_DTYPE_F32
         self.dtype = dt
         self.shapes = [_abi.cb_attn_shape(step.Hq, step.Hkv, step.D, step.P, dt, scheduler.windows[l], decode_split,
-                                          prefill_split) for l in range(self.n_layers)]
+                                          prefill_split, prefill_rows) for l in range(self.n_layers)]
         for L in step.layers:
             check_dtypes(AttnPlan(None, self.shapes[0], None), q=L.q, out=L.out, k_cache=L.k_cache,
                          v_cache=L.v_cache, k_new=L.k_new, v_new=L.v_new)
@@ -326,7 +326,9 @@ class StepPipeline:
             padded.num_tokens = Tp
             self._check_workspace(l, padded)
             views.append((base + 4 * bt_at, wp, base + 4 * sm_at, padded, base + 4 * pl_at, base + 4 * cnt_at, Tp))
-        return lo, at, views, (i, Tp, Np, tuple(widths), tuple(caps))
+        # the prefill tile size picks the prefill kernel's work-group shape: part of the launch, so part of the key
+        tiles = tuple(int(p.info.prefill_tokens) for p, _ in plans)
+        return lo, at, views, (i, Tp, Np, tuple(widths), tuple(caps), tiles)
 
     def prepare(self):
         """Host half of a step: schedule + plan into the next pinned buffer and enqueue its copy to the device.

@@ -57,6 +57,20 @@ def test_reduced_workload_all_rows_and_pages(torch_gpu, idx, fused):
         _check_pages(w, st, l)
 
 
+@pytest.mark.parametrize("idx", [3, 5])
+def test_reduced_workload_wide_prefill_tiles(torch_gpu, idx):
+    """The reduced mixed step and layer pair with 256-row prefill tiles (8-wave work groups) forced: every row and
+    every page."""
+    w = make_workload(idx, mini=True)
+    st = _run(w, fused=True, prefill_rows=256)
+    G = w.Hq // w.Hkv
+    assert all(L.plan.info.prefill_tokens * G == 256 for L in st.layers if L.plan.info.n_prefill)
+    for l in range(len(w.layers)):
+        mx, mean = H.compare(w, st, l, label=f"w{idx} reduced layer {l}")
+        print(f"  layer {l}: max {mx:.3g} mean {mean:.3g}", flush=True)
+        _check_pages(w, st, l)
+
+
 def _sample_tokens(sched, rng, n_dec=12, per_chunk=6):
     qsl = sched["query_start_loc"]
     seq = sched["seq_lens"]
@@ -162,15 +176,16 @@ EDGE = {
 }
 
 
-@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("fused,rows", [(False, 0), (True, 0), (True, 256)])
 @pytest.mark.parametrize("name", list(EDGE))
-def test_edge_cases(torch_gpu, name, fused):
+def test_edge_cases(torch_gpu, name, fused, rows):
+    """Each edge case with the append as its own launch and fused, and fused with 256-row prefill tiles."""
     cfg = dict(EDGE[name])
     reqs = cfg.pop("reqs")
     ds = cfg.pop("decode_split", 0)
     ps = cfg.pop("prefill_split", 0)
     w = H.custom_workload(reqs, name=name, **cfg)
-    st = _run(w, fused=fused, decode_split=ds, prefill_split=ps)
+    st = _run(w, fused=fused, decode_split=ds, prefill_split=ps, prefill_rows=rows)
     print(f"  plan {st.layers[0].plan.counts()}", flush=True)
     H.compare(w, st, 0, label=name)
     _check_pages(w, st, 0)

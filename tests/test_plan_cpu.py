@@ -69,8 +69,12 @@ def test_plan_covers_every_row_exactly_once(seed):
     P = int(rng.choice([2, 8, 16, 32]))
     ds = int(rng.choice([0, 64, 256]))
     ps = int(rng.choice([0, 64, 512]))
-    plan = cb.plan_attention(qsl, seq, ring, Hkv * G, Hkv, 128, P, dtype, window, ds, ps)
+    rows = int(rng.choice([0, 128, 256]))
+    plan = cb.plan_attention(qsl, seq, ring, Hkv * G, Hkv, 128, P, dtype, window, ds, ps, rows)
     _cover_check(qsl, seq, ring, plan, window)
+    if plan.info.n_prefill:
+        assert plan.info.prefill_tokens * G == (rows or plan.info.prefill_tokens * G)
+        assert plan.info.prefill_tokens * G in (128, 256)
     c = plan.counts()
     fast = dtype == "bf16" and P >= 8
     if not fast:
@@ -93,6 +97,25 @@ def test_plan_of_workloads(idx):
         assert plan.info.max_page_index < s["layers"][l]["width"]
         if w.dtype == "f32":
             assert plan.counts()["rowwise"] >= s["num_tokens"]
+
+
+def test_prefill_rows_choice():
+    """256-row tiles when the chunks give at least three such work groups per CU (256 CUs), else 128; a
+    requested size is honoured."""
+    G, Hkv = 4, 8
+    big = [0, 2048, 4096, 6144, 8064]                   # three 2048-token chunks and a 1920-token one: 126 tiles
+    seq = [6144, 14336, 18432, 1920]
+    plan = cb.plan_attention(big, seq, None, G * Hkv, Hkv, 128, 32, "bf16")
+    assert plan.info.prefill_tokens * G == 256
+    small = [0, 512, 1024]                              # 16 tiles x 8 heads: far fewer than 3 per CU
+    plan = cb.plan_attention(small, [4096, 512], None, G * Hkv, Hkv, 128, 32, "bf16")
+    assert plan.info.prefill_tokens * G == 128
+    for rows in (128, 256):
+        plan = cb.plan_attention(small, [4096, 512], None, G * Hkv, Hkv, 128, 32, "bf16", -1, 0, 0, rows)
+        assert plan.info.prefill_tokens * G == rows
+        _cover_check(np.array(small), np.array([4096, 512]), None, plan, -1)
+    with pytest.raises(cb.CbError):
+        cb.plan_attention(small, [4096, 512], None, G * Hkv, Hkv, 128, 32, "bf16", -1, 0, 0, 192)
 
 
 def test_plan_rejects_bad_input():
