@@ -108,8 +108,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // consecutive, R-aligned offsets of one page (the usual case inside a prefill chunk) gives every d-row of that page
 // R contiguous elements, written as 16-byte stores. With R = 16 both halves of a 32-byte d-row come from the same
 // work group, so whole 32-byte pieces of memory are written. Tokens outside such runs are written element by
-// element. Tokens whose slot is negative or outside the pool are skipped. A work group's first loads of new rows go
-// out together with its slot reads (they do not depend on them), so it waits for memory about once.
+// element. Tokens whose slot is negative or outside the pool are skipped.
 
 constexpr int kAppendGroup = 16;
 constexpr int kAppendThreads = 256;
@@ -126,41 +125,6 @@ __device__ __forceinline__ void append_group(T *__restrict__ kc, T *__restrict__
     const int nt = int(min(int64_t(TG), int64_t(num_tokens) - t0));
     const int64_t pool = int64_t(num_pages) * P;
     const int R = min(TG, P);
-    const int cpr = D / E;             // 16-byte chunks per K row
-    const int nk = nt * cpr;           // K chunks
-    const int nv = (TG / E) * D;       // V chunks of E tokens (a wave covers 64 consecutive d of one chunk row)
-    // A pass moves one K chunk and one V chunk per thread. Its loads do not depend on the slots, so the first
-    // pass's loads are issued before the slots are read: the work group then waits for memory about once.
-    auto load_pass = [&](int c, u32x4 &kval, T (&vals)[E]) {
-        kval = u32x4{0, 0, 0, 0};
-        if (c < nk) kval = load16(kn + ((t0 + c / cpr) * Hkv + g) * D + int64_t(c % cpr) * E);
-        const int i0 = (c / D) * E, d = c % D;
-        const bool vact = c < nv && i0 < nt;
-#pragma unroll
-        for (int e = 0; e < E; ++e) vals[e] = (vact && i0 + e < nt) ? vn[((t0 + i0 + e) * Hkv + g) * D + d] : T(0);
-    };
-    auto store_pass = [&](int c, const u32x4 &kval, const T (&vals)[E]) {
-        if (c < nk) {
-            const int i = c / cpr, cc = c % cpr;
-            const int64_t slot = s_slot[i];
-            if (slot >= 0) store16(kc + ((slot / P * Hkv + g) * P + slot % P) * D + int64_t(cc) * E, kval);
-        }
-        const int i0 = (c / D) * E, d = c % D;
-        if (c >= nv || i0 >= nt) return;
-        if (s_run[i0 / R]) {
-            const int64_t s0 = s_slot[i0];
-            store16(vc + ((s0 / P * Hkv + g) * D + d) * P + s0 % P, *reinterpret_cast<const u32x4 *>(vals));
-        } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int64_t slot = i0 + e < nt ? s_slot[i0 + e] : -1;
-                if (slot >= 0) vc[((slot / P * Hkv + g) * D + d) * P + slot % P] = vals[e];
-            }
-        }
-    };
-    u32x4 kval;
-    T vals[E];
-    load_pass(int(threadIdx.x), kval, vals);
     if (threadIdx.x < TG) {
         int64_t sl = threadIdx.x < nt ? int64_t(slots[t0 + threadIdx.x]) : -1;
         s_slot[threadIdx.x] = (sl >= 0 && sl < pool) ? sl : -1;
@@ -174,10 +138,42 @@ __device__ __forceinline__ void append_group(T *__restrict__ kc, T *__restrict__
         s_run[threadIdx.x] = ok;
     }
     __syncthreads();
-    store_pass(int(threadIdx.x), kval, vals);
-    for (int c = int(blockDim.x + threadIdx.x); c - int(threadIdx.x) < max(nk, nv); c += int(blockDim.x)) {
-        load_pass(c, kval, vals);
-        store_pass(c, kval, vals);
+    // Each pass issues all of a thread's loads (one K chunk; E tokens of one V d-row, a wave covering 64
+    // consecutive d) before its stores, so a work group waits for memory about once per pass.
+    const int cpr = D / E;             // 16-byte chunks per K row
+    const int nk = nt * cpr;           // K chunks
+    const int nv = (TG / E) * D;       // V chunks of E tokens
+    for (int base = 0; base < max(nk, nv); base += blockDim.x) {
+        const int c = base + int(threadIdx.x);
+        u32x4 kval = {0, 0, 0, 0};
+        int64_t kdst = -1;
+        if (c < nk) {
+            const int i = c / cpr, cc = c % cpr;
+            const int64_t slot = s_slot[i];
+            if (slot >= 0) {
+                kval = load16(kn + ((t0 + i) * Hkv + g) * D + int64_t(cc) * E);
+                kdst = ((slot / P * Hkv + g) * P + slot % P) * D + int64_t(cc) * E;
+            }
+        }
+        const int qa = c / D, d = c % D;
+        const int i0 = qa * E;   // first token of the V chunk
+        const bool vact = c < nv && i0 < nt;
+        T vals[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            vals[e] = (vact && i0 + e < nt) ? vn[((t0 + i0 + e) * Hkv + g) * D + d] : T(0);
+        if (kdst >= 0) store16(kc + kdst, kval);
+        if (!vact) continue;
+        if (s_run[i0 / R]) {
+            const int64_t s0 = s_slot[i0];
+            store16(vc + ((s0 / P * Hkv + g) * D + d) * P + s0 % P, *reinterpret_cast<const u32x4 *>(vals));
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int64_t slot = i0 + e < nt ? s_slot[i0 + e] : -1;
+                if (slot >= 0) vc[((slot / P * Hkv + g) * D + d) * P + slot % P] = vals[e];
+            }
+        }
     }
 }
 

@@ -518,7 +518,11 @@ extern "C" cb_status cb_plan_attention(const int32_t *qsl, const int32_t *seq_le
                 const int32_t qc = std::min(tile_tokens, q - i0);
                 const int64_t pos0 = ctx + i0;
                 const int64_t lo = lo_of(pos0), hi = pos0 + qc;
-                const int64_t first = (lo / PS) * PS;
+                // split boundaries: at multiples of a caller-fixed PS, so that a request's split points (and its
+                // output bits) do not depend on the rest of the batch; with the planner's own PS, from the tile's
+                // first 64-key tile, so that a tile whose keys fit one split is never cut (a sliding window's range
+                // would otherwise straddle a multiple of PS)
+                const int64_t first = sh->prefill_split > 0 ? (lo / PS) * PS : (lo / 64) * 64;
                 const int64_t n = ceil_div(hi - first, PS);
                 const int64_t base = n > 1 ? slots : -1;
                 for (int64_t s = 0; s < n; ++s) {
