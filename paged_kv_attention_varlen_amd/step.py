@@ -14,7 +14,7 @@ from typing import List, Optional
 
 import numpy as np
 
-from .hip_events import HipEvent
+from .hip_events import HipEvent, memcpy_h2d_async
 from . import (CB_LAYOUT_KD_VT, CB_PHASE_COMBINE, CB_PHASE_DECODE, CB_PHASE_PREFILL, CB_PHASE_ROWWISE, AttnPlan,
                CB_E_CAPACITY, CbError, Scheduler, _abi, check_dtypes, kv_append, paged_attention, plan_into,
                schedule_arrays)
@@ -156,7 +156,8 @@ class StepPipeline:
         self.aux = torch.cuda.Stream(dev) if concurrent else None
         self.copier = torch.cuda.Stream(dev) if copy_stream else None
         # events are created once (torch creates the HIP event at its first record) and re-recorded every step
-        self.copy_ev = [torch.cuda.Event(), torch.cuda.Event()]   # copy into buffer pair i finished
+        # copy into buffer pair i finished: the kernels read what it copied, so it keeps the system-scope fence
+        self.copy_ev = [HipEvent(), HipEvent()]
         # last kernels reading device buffer i finished: it only orders the next copy into that buffer after reads,
         # so it is recorded without the system-scope fence
         self.rel_ev = [HipEvent(system_fence=False), HipEvent(system_fence=False)]
@@ -171,6 +172,7 @@ class StepPipeline:
         self.lib = _abi.load()
         self.h_main = C.c_void_p(self.main.cuda_stream)
         self.h_aux = C.c_void_p(self.aux.cuda_stream) if self.aux is not None else None
+        self.h_copier = C.c_void_p(self.copier.cuda_stream) if self.copier is not None else None
         self.args = []
         for l, L in enumerate(step.layers):
             a = _abi.cb_attn_args()
@@ -333,7 +335,6 @@ class StepPipeline:
     def prepare(self):
         """Host half of a step: schedule + plan into the next pinned buffer and enqueue its copy to the device.
         Returns the per-layer launch views (block table, width, slot mapping, plan header, plan, counts, tokens)."""
-        torch = _torch()
         i = self.k % 2
         if self.copied[i] is not None:
             self.copied[i].synchronize()   # the pinned half of pair i is free again
@@ -356,20 +357,19 @@ class StepPipeline:
         if self.keep_schedule:
             self.last_schedule = schedule_arrays(self.host[i].numpy(), hs, self.n_layers)
         self.num_tokens = hs.num_tokens
-        dev = self.dev[i]
         ev = self.copy_ev[i]
+        dst, src, nbytes = self.dev[i].data_ptr() + 4 * lo, self.host[i].data_ptr() + 4 * lo, 4 * (hi - lo)
         if self.copier is not None:
             # the copy waits only for the step that last read this device buffer, then runs beside the kernels of
             # the step in flight; the compute stream waits for it before this step's first kernel
             if self.released[i] is not None:
-                self.released[i].wait(self.copier)
-            with torch.cuda.stream(self.copier):
-                dev[lo:hi].copy_(self.host[i][lo:hi], non_blocking=True)
-            ev.record(self.copier)
-            self.main.wait_event(ev)
+                self.released[i].wait_on(self.h_copier)
+            memcpy_h2d_async(dst, src, nbytes, self.h_copier)
+            ev.record_on(self.h_copier)
+            ev.wait_on(self.h_main)
         else:
-            dev[lo:hi].copy_(self.host[i][lo:hi], non_blocking=True)
-            ev.record(self.main)
+            memcpy_h2d_async(dst, src, nbytes, self.h_main)
+            ev.record_on(self.h_main)
         self.copied[i] = ev
         self.cur = i
         self.key = key
@@ -466,5 +466,5 @@ class StepPipeline:
             self._launch(views, main, self.h_main, events)
         if self.copier is not None:
             rel = self.rel_ev[self.cur]
-            rel.record(main)
+            rel.record_on(self.h_main)
             self.released[self.cur] = rel
