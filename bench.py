@@ -400,7 +400,7 @@ def main():
                          "known-size reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU "
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the library has no multi-GPU "
               "path: the step would shard by kv heads or by requests with no exchange inside attention)",
               file=sys.stderr)
         sys.exit(2)

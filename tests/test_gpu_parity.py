@@ -250,8 +250,8 @@ def test_prefill_first_step(torch_gpu):
             _check_pages(w, st, l)
 
 
-PIPELINE_MODES = ["copy stream", "copy on compute stream", "concurrent prefill", "graph replay", "separate append",
-                  "per-phase launches with events"]
+PIPELINE_MODES = ["copy stream", "copy on compute stream", "concurrent prefill", "graph replay",
+                  "graph replay, 256-row prefill tiles", "separate append", "per-phase launches with events"]
 
 
 @pytest.mark.parametrize("mode", PIPELINE_MODES)
@@ -265,9 +265,10 @@ def test_pipeline_steps_match_oracle(torch_gpu, mode):
     for idx in (3, 5):
         w = make_workload(idx, mini=True)
         st = build_step(w)
+        graphs = mode.startswith("graph replay")
         pipe = pipeline_for(w, st, copy_stream=(mode != "copy on compute stream"),
-                            concurrent=(mode == "concurrent prefill"), graphs=(mode == "graph replay"),
-                            fused_append=(mode != "separate append"))
+                            concurrent=(mode == "concurrent prefill"), graphs=graphs,
+                            fused_append=(mode != "separate append"), prefill_rows=(256 if "256" in mode else 0))
         events = None
         if mode == "per-phase launches with events":   # the benchmark's timing events (no system-scope fence)
             from paged_kv_attention_varlen_amd.hip_events import HipEvent
@@ -284,7 +285,7 @@ def test_pipeline_steps_match_oracle(torch_gpu, mode):
                 H.compare(w, st, l, label=f"pipeline {mode} w{idx} layer {l} repetition {rep}")
         for l in range(len(w.layers)):
             _check_pages(w, st, l)
-        if mode == "graph replay":
+        if graphs:
             assert pipe.captures == 2 and pipe.replays == 5, "one graph per metadata buffer of the padded shape"
         if events is not None:   # the events bracketed the decode, prefill and merge launches of the last step
             for l in range(len(w.layers)):
