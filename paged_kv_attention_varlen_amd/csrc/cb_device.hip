@@ -617,6 +617,9 @@ __global__ __launch_bounds__(64) void rowwise_kernel(const T *__restrict__ q, T 
 // Softmax in the log2 domain with a lazily moved running maximum: the weights are computed speculatively against the
 // current maximum, and only when some row's weights could exceed 2^8 (its sum does) does a rare path move
 // it, rescale that row's accumulators and recompute the weights. Tiles every row sees completely skip the mask.
+// Q is multiplied by scale * log2(e) once, when it is loaded, and rounded to bf16; the score accumulators start at
+// -mu (mu: the running maximum, 0 before the row has one), so the QK product yields each weight's exponent and the
+// common path spends one exp2 and no other arithmetic per score.
 
 constexpr int kPfKeys = 64;    // keys per tile
 constexpr int kPrefillMaxPages = 1536;   // page ids of one prefill item staged in LDS (split / page + 2)
@@ -788,17 +791,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             for (int kb = 0; kb < KB; ++kb) {
                 u32x4 v = {0, 0, 0, 0};
                 if (ok) v = load16(qrow + 16 * kb);
-                qf[kb] = as_bf16x8(v);
+                const bf16x8 raw = as_bf16x8(v);
+                bf16x8 sc;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sc[e] = static_cast<__bf16>(static_cast<float>(raw[e]) * scale_log2e);
+                qf[kb] = sc;
             }
         }
+        // the score accumulators start at -mu_c, so that S = scale log2(e) q.k - mu_c is the exponent of the weight;
+        // mu_c is the running maximum m, or 0 while the row has none
+        float mu_c = 0.f;
+        f32x16 cm;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) cm[v] = 0.f;
         // S^T of one 32-key half
         auto qk_half = [&](const uint8_t *kbuf, int s, f32x16 &S) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) S[v] = 0.f;
-#pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 const bf16x8 a = as_bf16x8(load16(kbuf + k_rd + (s * NK + kb / 2) * 2048 + (kb & 1) * 512));
-                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], S, 0, 0, 0);
+                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], kb == 0 ? cm : S, 0, 0, 0);
             }
         };
         // O^T += V^T P^T over one 32-key half (k-steps 2s, 2s+1)
@@ -819,14 +830,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             for (int v = 0; v < 16; ++v)
                 if (unsigned(base + 16 * (v >> 3) + (v & 7)) > unsigned(rspan)) S[v] = kNegInf;
         };
-        auto weights = [&](const f32x16 &S, float mu, bf16x8 (&pf)[2]) {
+        auto weights = [&](const f32x16 &S, float delta, bool shift, bf16x8 (&pf)[2]) {
             float sum = 0.f;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 bf16x8 p;
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    p[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(S[8 * kk + e], scale_log2e, -mu)));
+                    p[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(shift ? S[8 * kk + e] + delta : S[8 * kk + e]));
                 pf[kk] = p;
                 sum = sum_bf16x8(p, sum);
             }
@@ -838,7 +849,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // that climbed past the running maximum) the rare path below settles the row. No row maximum is computed on
         // the common path.
         auto softmax_half = [&](const f32x16 &S, bf16x8 (&pf)[2], float &lsum) {
-            lsum = weights(S, m == kNegInf ? 0.f : m, pf);
+            lsum = weights(S, 0.f, false, pf);
             // pin the speculative results here, beside the matrix work of this region: otherwise the compiler sinks
             // them past the rare-path branch that follows and they no longer overlap the MFMAs
 #pragma unroll
@@ -853,7 +864,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         };
         // Rare path for the rows that asked for it: take the half's true row maximum (both lanes of the row), move
         // the running maximum up to it if it is higher, rescale the row's accumulators and recompute its weights.
-        auto settle = [&](bool want, f32x16 &S, bf16x8 (&pf)[2], float &lsum) {
+        // Scores already computed against the old mu_c (this half, and `other`: the tile's second half when the first
+        // is settled) are shifted to the new one, and later tiles' accumulators start at the new -mu_c.
+        auto settle = [&](bool want, f32x16 &S, bf16x8 (&pf)[2], float &lsum, f32x16 *other) {
             // a loop of at most one trip rather than a branch, so that the compiler keeps the rescale out of line
             const int trips = __builtin_amdgcn_ballot_w64(want) ? 1 : 0;
 #pragma nounroll
@@ -862,7 +875,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
                 for (int v = 1; v < 16; ++v) x = __builtin_elementwise_maximum(x, S[v]);
                 // the partner lane of the row decides too: both see the same maximum
-                const float tmax = max_xor32(x) * scale_log2e;
+                const float tmax = max_xor32(x) + mu_c;
                 const bool bump = __shfl_xor(int(want), 32) != 0 || want;
                 const float m_new = bump ? fmaxf(m, tmax) : m;
                 const float alpha = m_new > m ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
@@ -870,7 +883,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
                 for (int b = 0; b < DB; ++b) acc[b] *= alpha;
                 m = m_new;
-                lsum = weights(S, m_new == kNegInf ? 0.f : m_new, pf);
+                const float mu_new = m_new == kNegInf ? 0.f : m_new;
+                const float delta = mu_c - mu_new;
+                lsum = weights(S, delta, true, pf);
+                if (other) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) (*other)[v] += delta;
+                }
+                mu_c = mu_new;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) cm[v] = -mu_c;
             }
             l += lsum;
         };
@@ -894,11 +916,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             if (edge) mask_half(S0, tile * kPfKeys);
             qk_half(kcur, 1, S1);
             const bool b0 = softmax_half(S0, p0, ls0);
-            settle(b0, S0, p0, ls0);
+            settle(b0, S0, p0, ls0, &S1);
             if (edge) mask_half(S1, tile * kPfKeys + 32);
             pv_half(vcur, 0, p0);
             const bool b1 = softmax_half(S1, p1, ls1);
-            settle(b1, S1, p1, ls1);
+            settle(b1, S1, p1, ls1, nullptr);
             pv_half(vcur, 1, p1);
             __builtin_amdgcn_s_setprio(0);
             // the next tile has landed for every wave; every wave is done with this one
