@@ -13,8 +13,9 @@ The headline is the largest single-GPU workload: the hybrid full + sliding-windo
 mixed step (128 decodes with context up to 32768, three 2048-token continuing chunks and a 1920-token new prompt;
 32 query / 8 kv heads, head_dim 128, bf16, page 32, window 4096). Exactly W untimed warm-up steps, then K timed
 steps between two device synchronisations: `value` is query tokens per second over those K steps (wall clock).
-Per-kernel durations come from fence-free HIP events recorded on the compute stream around the decode, prefill and
-merge launches of every EVENTS_EVERY-th timed step. A second pass of steps, each bracketed by step-boundary events,
+Per-kernel durations come from fence-free HIP events that the decode, prefill and merge launches of every
+EVENTS_EVERY-th timed step record themselves as their kernels start and end (cb_attn_args.timing_start /
+timing_stop), so that they time the kernels as a kernel trace does. A second pass of steps, each bracketed by step-boundary events,
 gives the p10/p50/p90 step times; a third runs steps after a 1 GiB write (larger than the 256 MB last-level cache)
 and reports the kernels' rooflines without a warm cache; a fourth times the same step with the prefill kernels on a
 second stream beside the decode kernel (only its step time: the kernels then share the GPU). The mixed 2048-token
@@ -265,10 +266,9 @@ def measure(index: int, steps: int, warmup: int, args, dist_steps: int, flush_st
     torch.cuda.synchronize()
     L = len(w.layers)
     main = pipe.main
-    # Every EVENTS_EVERY-th timed step brackets its decode, prefill and merge kernels with events (6 per layer); the
-    # kernel averages come from that sample of the timed steps. The timing events are recorded without the
-    # system-scope fence (hipEventDisableSystemFence): they order nothing, and the cache write-back and invalidation
-    # of that fence would otherwise be charged to the kernel that follows the event.
+    # Every EVENTS_EVERY-th timed step brackets its decode, prefill and merge kernels with events (6 per layer), which
+    # the kernels record as they start and end; the kernel averages come from that sample of the timed steps. The
+    # events are created without the system-scope fence (hipEventDisableSystemFence): they order nothing.
     timed = list(range(0, steps, EVENTS_EVERY))
     events = {k: [[HipEvent(timing=True, system_fence=False) for _ in range(6)] for _ in range(L)] for k in timed}
     for per_step in events.values():

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 6
+#define CB_ABI_VERSION 7
 
 typedef int32_t cb_status;
 #define CB_OK 0
@@ -345,6 +345,13 @@ typedef struct cb_attn_args {
      * Everything else the launches read (plan items, block table, slot mapping) is read from device memory too,
      * so one captured launch serves every step whose metadata is written to the same addresses. */
     const int32_t *counts;
+    /* Optional timing events (hipEvent_t created with timing enabled), for callers that time the kernels: the call's
+     * first kernel records timing_start when it begins executing and its last kernel records timing_stop when it
+     * ends, so that the pair brackets the kernels alone. Events recorded on the stream around the call would also
+     * count the dispatch after the previous work and the completion signal after the last kernel. A call that
+     * launches no kernel (its phases have no items) records both on the stream. NULL: none. */
+    void *timing_start;
+    void *timing_stop;
 } cb_attn_args;
 
 #define CB_PHASE_DECODE 1         /* split-KV decode kernel                                                     */

@@ -13,7 +13,7 @@ CB_DECODING, CB_PREFILLING, CB_WAITING = 0, 1, 2
 CB_MAX_LAYERS = 2
 CB_PHASE_DECODE, CB_PHASE_ROWWISE, CB_PHASE_PREFILL, CB_PHASE_COMBINE = 1, 2, 4, 8
 CB_POLICY_FIFO, CB_POLICY_PREFILL_FIRST = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 CB_LAYOUT_PAGED_NHD, CB_LAYOUT_KD_VT = 0, 1
 CB_NOALLOC_WORKSPACE_BYTES = 96 << 20
 
@@ -68,7 +68,8 @@ class cb_attn_args(C.Structure):
                 ("shape", cb_attn_shape), ("num_pages", C.c_int32), ("table_width", C.c_int32),
                 ("scale", C.c_float), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
                 ("phases", C.c_int32), ("k_new", C.c_void_p), ("v_new", C.c_void_p), ("slot_mapping", C.c_void_p),
-                ("num_new", C.c_int32), ("counts", C.c_void_p)]
+                ("num_new", C.c_int32), ("counts", C.c_void_p), ("timing_start", C.c_void_p),
+                ("timing_stop", C.c_void_p)]
 
 
 EXPORTS = ("cb_build_metadata", "cb_slot_mapping", "cb_validate_metadata", "cb_plan_attention", "cb_kv_append", "cb_kv_copy_pages", "cb_paged_attention", "cb_paged_attention_noalloc",

@@ -10,6 +10,7 @@
 // Softmax runs in the log2 domain: scores are multiplied by scale*log2(e) once and exponentiated with exp2;
 // partial results store the running maximum in those units.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -1047,22 +1048,40 @@ bool shape_ok(const cb_attn_shape &s) {
 
 }  // namespace
 
-// Launch of the append kernel over all tokens (sizes already checked).
+// A kernel launch on stream `s`, the call's launch number `k_launch` of `n_launch`. The call's first kernel records
+// the caller's start event when it begins executing and its last kernel the stop event when it ends
+// (hipExtLaunchKernel), so that the pair times the kernels themselves: events recorded on the stream around the call
+// would also count the dispatch after the previous work and the completion signal after the last kernel.
+#define CB_LAUNCH(K, GRID, BLOCK, ...)                                                                         \
+    do {                                                                                                       \
+        hipEvent_t ev_a = k_launch == 0 ? ev_start : nullptr;                                                  \
+        hipEvent_t ev_b = k_launch == n_launch - 1 ? ev_stop : nullptr;                                        \
+        if (ev_a || ev_b)                                                                                      \
+            hipExtLaunchKernelGGL(K, GRID, BLOCK, 0, s, ev_a, ev_b, 0, __VA_ARGS__);                           \
+        else                                                                                                   \
+            hipLaunchKernelGGL(K, GRID, BLOCK, 0, s, __VA_ARGS__);                                              \
+        ++k_launch;                                                                                            \
+    } while (0)
+
+// Launch of the append kernel over all tokens (sizes already checked); the events as for CB_LAUNCH, with this
+// launch as a call's only one.
 static hipError_t launch_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new, const int32_t *slots,
                          int32_t num_tokens, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
-                         int32_t head_dim, int32_t dtype, hipStream_t s) {
+                         int32_t head_dim, int32_t dtype, hipStream_t s, hipEvent_t ev_start = nullptr,
+                         hipEvent_t ev_stop = nullptr) {
+    int k_launch = 0;
+    const int n_launch = 1;
     const int64_t groups = (int64_t(num_tokens) + kAppendGroup - 1) / kAppendGroup;
     const dim3 grid{static_cast<unsigned>(groups), static_cast<unsigned>(num_kv_heads), 1u};
     if (dtype == CB_DTYPE_F32) {
-        hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(kAppendThreads), 0, s,
-                           static_cast<float *>(k_cache), static_cast<float *>(v_cache),
-                           static_cast<const float *>(k_new), static_cast<const float *>(v_new), slots,
-                           num_tokens, num_pages, page_size, num_kv_heads, head_dim);
+        CB_LAUNCH(kv_append_kernel<float>, grid, dim3(kAppendThreads), static_cast<float *>(k_cache),
+                  static_cast<float *>(v_cache), static_cast<const float *>(k_new),
+                  static_cast<const float *>(v_new), slots, num_tokens, num_pages, page_size, num_kv_heads, head_dim);
     } else {
-        hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(kAppendThreads), 0, s,
-                           static_cast<uint16_t *>(k_cache), static_cast<uint16_t *>(v_cache),
-                           static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new), slots,
-                           num_tokens, num_pages, page_size, num_kv_heads, head_dim);
+        CB_LAUNCH(kv_append_kernel<uint16_t>, grid, dim3(kAppendThreads), static_cast<uint16_t *>(k_cache),
+                  static_cast<uint16_t *>(v_cache), static_cast<const uint16_t *>(k_new),
+                  static_cast<const uint16_t *>(v_new), slots, num_tokens, num_pages, page_size, num_kv_heads,
+                  head_dim);
     }
     return hipGetLastError();
 }
@@ -1121,7 +1140,12 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
     if (pl.n_decode < 0 || pl.n_prefill < 0 || pl.n_rowwise < 0 || pl.n_combine < 0 || pl.n_partials < 0)
         return CB_E_INVAL;
     const int64_t n_work = int64_t(pl.n_decode) + pl.n_prefill + pl.n_rowwise + pl.n_combine;
-    if (n_work == 0) return CB_OK;
+    if (n_work == 0) {   // nothing to launch: the timing events are recorded where the kernels would have run
+        for (void *ev : {a->timing_start, a->timing_stop})
+            if (ev && hipEventRecord(static_cast<hipEvent_t>(ev), static_cast<hipStream_t>(stream)) != hipSuccess)
+                return CB_E_HIP;
+        return CB_OK;
+    }
     if (!a->out || !a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->plan) return CB_E_INVAL;
     if (a->num_pages < 1 || a->table_width <= pl.max_page_index) return CB_E_INVAL;
     const int Hq = sh.num_q_heads, Hkv = sh.num_kv_heads, D = sh.head_dim;
@@ -1148,6 +1172,7 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
                                                       align256(size_t(pl.n_partials) * Hq * D * sizeof(float)))
                           : nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t ev_start = static_cast<hipEvent_t>(a->timing_start), ev_stop = static_cast<hipEvent_t>(a->timing_stop);
     const int Pl = ilog2(sh.page_size);
     const float sl2e = a->scale * 1.4426950408889634f;   // scale * log2(e): softmax in base 2
     const int32_t *plan = a->plan;
@@ -1155,9 +1180,16 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
                                       : a->phases;
 
     const bool append_here = fuse && (ph & first_reader) != 0;
+    // the launches this call makes, in order (the timing events go to the first and the last)
+    const bool l_dec = pl.n_decode > 0 && (ph & CB_PHASE_DECODE);
+    const bool l_row = pl.n_rowwise > 0 && (ph & CB_PHASE_ROWWISE);
+    const bool l_pre = pl.n_prefill > 0 && (ph & CB_PHASE_PREFILL);
+    const bool l_com = pl.n_combine > 0 && (ph & CB_PHASE_COMBINE);
+    const int n_launch = int(l_dec) + int(!l_dec && append_here) + int(l_row) + int(l_pre) + int(l_com);
+    int k_launch = 0;
     const int64_t append_groups = append_here ? (int64_t(a->num_new) + kAppendGroup - 1) / kAppendGroup * Hkv : 0;
     if (int64_t(pl.n_decode) * Hkv + append_groups > INT32_MAX) return CB_E_UNSUPPORTED;
-    if (pl.n_decode > 0 && (ph & CB_PHASE_DECODE)) {
+    if (l_dec) {
         // with the fused append, its work groups follow the decode work groups in the same grid
         const int n_dec = pl.n_decode * Hkv;
         const dim3 grid{unsigned(n_dec + append_groups), 1u, 1u};
@@ -1171,26 +1203,29 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
         const uint16_t *vn = append_here ? static_cast<const uint16_t *>(a->v_new) : nullptr;
         const int32_t *sm = append_here ? a->slot_mapping : nullptr;
         if (D == 128)
-            hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,
-                               a->table_width, a->num_pages, plan + pl.off_decode, part_o, part_ml, Hq, Hkv, Pl, sl2e,
-                               n_dec, kw, vw, kn, vn, sm, a->num_new, a->counts);
+            CB_LAUNCH(decode_kernel<128>, grid, dim3(256), qq, oo, kk, vv, a->block_table, a->table_width,
+                      a->num_pages, plan + pl.off_decode, part_o, part_ml, Hq, Hkv, Pl, sl2e, n_dec, kw, vw, kn, vn, sm,
+                      a->num_new, a->counts);
         else
-            hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table,
-                               a->table_width, a->num_pages, plan + pl.off_decode, part_o, part_ml, Hq, Hkv, Pl, sl2e,
-                               n_dec, kw, vw, kn, vn, sm, a->num_new, a->counts);
+            CB_LAUNCH(decode_kernel<64>, grid, dim3(256), qq, oo, kk, vv, a->block_table, a->table_width,
+                      a->num_pages, plan + pl.off_decode, part_o, part_ml, Hq, Hkv, Pl, sl2e, n_dec, kw, vw, kn, vn, sm,
+                      a->num_new, a->counts);
     } else if (append_here) {
         // the plan's first cache reader is the per-token or the prefill kernel: append on its own launch first
-        if (launch_append(const_cast<void *>(a->k_cache), const_cast<void *>(a->v_cache), a->k_new, a->v_new,
-                          a->slot_mapping, a->num_new, a->num_pages, sh.page_size, Hkv, D, sh.dtype, s) != hipSuccess)
+        const hipError_t e = launch_append(const_cast<void *>(a->k_cache), const_cast<void *>(a->v_cache), a->k_new,
+                                           a->v_new, a->slot_mapping, a->num_new, a->num_pages, sh.page_size, Hkv, D,
+                                           sh.dtype, s, k_launch == 0 ? ev_start : nullptr,
+                                           k_launch == n_launch - 1 ? ev_stop : nullptr);
+        ++k_launch;
+        if (e != hipSuccess)
             return CB_E_HIP;
     }
-    if (pl.n_rowwise > 0 && (ph & CB_PHASE_ROWWISE)) {
+    if (l_row) {
         const dim3 grid(unsigned(pl.n_rowwise), unsigned(Hkv), unsigned((G + 15) / 16));
 #define CB_ROWWISE(T, DD)                                                                                         \
-    hipLaunchKernelGGL((rowwise_kernel<T, DD>), grid, dim3(64), 0, s, static_cast<const T *>(a->q),              \
-                       static_cast<T *>(a->out), static_cast<const T *>(a->k_cache),                           \
-                       static_cast<const T *>(a->v_cache), a->block_table, a->table_width, a->num_pages,        \
-                       plan + pl.off_rowwise, part_o, part_ml, Hq, Hkv, Pl, sl2e, a->counts)
+    CB_LAUNCH((rowwise_kernel<T, DD>), grid, dim3(64), static_cast<const T *>(a->q), static_cast<T *>(a->out),  \
+              static_cast<const T *>(a->k_cache), static_cast<const T *>(a->v_cache), a->block_table,          \
+              a->table_width, a->num_pages, plan + pl.off_rowwise, part_o, part_ml, Hq, Hkv, Pl, sl2e, a->counts)
         if (bf16) {
             if (D == 128) CB_ROWWISE(uint16_t, 128); else CB_ROWWISE(uint16_t, 64);
         } else {
@@ -1198,7 +1233,7 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
         }
 #undef CB_ROWWISE
     }
-    if (pl.n_prefill > 0 && (ph & CB_PHASE_PREFILL)) {
+    if (l_pre) {
         const dim3 grid(unsigned(xcd_grid(pl.n_prefill, Hkv)));
         const uint16_t *qq = static_cast<const uint16_t *>(a->q);
         uint16_t *oo = static_cast<uint16_t *>(a->out);
@@ -1207,13 +1242,13 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
         const bool wide = pf_rows == 256;   // 8-wave work groups
 #define CB_PREFILL(DD, PLOG)                                                                                   \
     if (wide)                                                                                                  \
-        hipLaunchKernelGGL((prefill_kernel<DD, PLOG, 8>), grid, dim3(512), 0, s, qq, oo, kk, vv, a->block_table, \
-                           a->table_width, a->num_pages, plan + pl.off_prefill, pl.n_prefill, part_o, part_ml, Hq, \
-                           Hkv, sl2e, sh.window_left, a->counts);                                            \
+        CB_LAUNCH((prefill_kernel<DD, PLOG, 8>), grid, dim3(512), qq, oo, kk, vv, a->block_table, a->table_width, \
+                  a->num_pages, plan + pl.off_prefill, pl.n_prefill, part_o, part_ml, Hq, Hkv, sl2e,             \
+                  sh.window_left, a->counts);                                                                  \
     else                                                                                                       \
-        hipLaunchKernelGGL((prefill_kernel<DD, PLOG, 4>), grid, dim3(256), 0, s, qq, oo, kk, vv, a->block_table, \
-                           a->table_width, a->num_pages, plan + pl.off_prefill, pl.n_prefill, part_o, part_ml, Hq, \
-                           Hkv, sl2e, sh.window_left, a->counts)
+        CB_LAUNCH((prefill_kernel<DD, PLOG, 4>), grid, dim3(256), qq, oo, kk, vv, a->block_table, a->table_width, \
+                  a->num_pages, plan + pl.off_prefill, pl.n_prefill, part_o, part_ml, Hq, Hkv, sl2e,             \
+                  sh.window_left, a->counts)
 #define CB_PREFILL_D(DD)                                                                                       \
     switch (Pl) {                                                                                              \
         case 3: CB_PREFILL(DD, 3); break;                                                                      \
@@ -1231,15 +1266,20 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
 #undef CB_PREFILL_D
 #undef CB_PREFILL
     }
-    if (pl.n_combine > 0 && (ph & CB_PHASE_COMBINE)) {
+    if (l_com) {
         const int heads_per_group = 256 / (D / 4);
         const dim3 grid(unsigned(pl.n_combine), unsigned((Hq + heads_per_group - 1) / heads_per_group));
         if (bf16)
-            hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s, static_cast<uint16_t *>(a->out),
-                               part_o, part_ml, plan + pl.off_combine, Hq, D, a->counts);
+            CB_LAUNCH(combine_kernel<uint16_t>, grid, dim3(256), static_cast<uint16_t *>(a->out), part_o, part_ml,
+                      plan + pl.off_combine, Hq, D, a->counts);
         else
-            hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, static_cast<float *>(a->out), part_o,
-                               part_ml, plan + pl.off_combine, Hq, D, a->counts);
+            CB_LAUNCH(combine_kernel<float>, grid, dim3(256), static_cast<float *>(a->out), part_o, part_ml,
+                      plan + pl.off_combine, Hq, D, a->counts);
+    }
+    // a call whose phases launch no kernel still records the timing events, where its kernels would have run
+    if (n_launch == 0) {
+        if (ev_start && hipEventRecord(ev_start, s) != hipSuccess) return CB_E_HIP;
+        if (ev_stop && hipEventRecord(ev_stop, s) != hipSuccess) return CB_E_HIP;
     }
     return hipGetLastError() == hipSuccess ? CB_OK : CB_E_HIP;
 }

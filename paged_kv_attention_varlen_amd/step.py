@@ -400,12 +400,12 @@ class StepPipeline:
             bt, width, sm, info, plan, counts, T = views[l]
             a = self.args[l]
             a.block_table, a.table_width, a.plan, a.plan_info, a.phases = bt, width, plan, info, phases
-            s = self.aux if aux else stream
-            if ev0 is not None:
-                ev0.record(s)
+            # the events are recorded by the call's first and last kernels as they start and end, so that the pair
+            # times the kernels, not the dispatch after the previous work or the completion signal after them
+            a.timing_start = ev0.handle if ev0 is not None else None
+            a.timing_stop = ev1.handle if ev1 is not None else None
             self._check(lib.cb_paged_attention(C.byref(a), self.h_aux if aux else handle), "cb_paged_attention")
-            if ev1 is not None:
-                ev1.record(s)
+            a.timing_start = a.timing_stop = None
 
         n = len(views)
         E = (lambda l, k: events[l][k]) if events else (lambda l, k: None)
