@@ -287,10 +287,19 @@ def test_pipeline_steps_match_oracle(torch_gpu, mode):
             _check_pages(w, st, l)
         if graphs:
             assert pipe.captures == 2 and pipe.replays == 5, "one graph per metadata buffer of the padded shape"
-        if events is not None:   # the events bracketed the decode, prefill and merge launches of the last step
+        if events is not None:
+            # the events were recorded by the first and last kernels of the decode, prefill and merge calls of the
+            # last step (or on the stream, for a call with nothing to launch): in stream order, and a call that ran
+            # kernels took time
             for l in range(len(w.layers)):
-                for a, b in ((0, 1), (2, 3), (4, 5)):
-                    assert events[l][a].elapsed_time(events[l][b]) >= 0.0
+                ev = events[l]
+                for k in range(5):
+                    assert ev[k].elapsed_time(ev[k + 1]) >= 0.0, (l, k)
+                c = st.layers[l].plan.counts()
+                for (a, b), n in (((0, 1), c["decode"]), ((2, 3), c["prefill"] + c["rowwise"]),
+                                  ((4, 5), c["combine"])):
+                    if n > 0:
+                        assert ev[a].elapsed_time(ev[b]) > 0.0, (l, a, n)
 
 
 def _append_slots(rng, P, n_pages, T):
