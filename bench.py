@@ -284,11 +284,14 @@ def measure(index: int, steps: int, warmup: int, args, dist_steps: int, flush_st
     ms_per_step = (t1 - t0) * 1e3 / steps
     log(f"[bench] workload {index}: {steps} steps {ms_per_step:.4f} ms/step")
 
-    def mean_us(a, b):
+    def mean_us(a, b, ran):
+        # a call that launched nothing recorded its two events back to back on the stream: reported as 0
         return [float(np.mean([events[k][l][a].elapsed_time(events[k][l][b]) for k in timed])) * 1e3
-                for l in range(L)]
+                if ran(step.layers[l].plan.counts()) else 0.0 for l in range(L)]
 
-    dec_us, pre_us, com_us = mean_us(0, 1), mean_us(2, 3), mean_us(4, 5)
+    dec_us = mean_us(0, 1, lambda c: c["decode"] > 0)
+    pre_us = mean_us(2, 3, lambda c: c["prefill"] + c["rowwise"] > 0 or (pipe.fused and c["decode"] == 0))
+    com_us = mean_us(4, 5, lambda c: c["combine"] > 0)
     work = algorithmic_work(w, sched)
     fused = pipe.fused and all(x["decodes"] for x in work)
     roofline, roofline_prefill = _rooflines(w, step, work, fused, dec_us, pre_us, len(timed))
