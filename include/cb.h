@@ -212,9 +212,14 @@ typedef struct cb_attn_shape {
     int32_t decode_split;      /* keys per decode split (a multiple of 64), 0 = chosen by the planner from the
                                   whole step's decode keys. Splits are merged in a fixed order, so a fixed value
                                   makes a request's output bits independent of the rest of its batch; with 0 they
-                                  may change with the batch (the values stay within rounding of each other)    */
+                                  may change with the batch (the values stay within rounding of each other).
+                                  On the decode kernel's path (bf16, pages of 8 or more keys, up to 16 grouped
+                                  heads) capped at 1038 pages of keys (rounded down to a multiple of 64), the
+                                  page ids it stages per split; the plan reports the size used                 */
     int32_t prefill_split;     /* keys per prefill-tile split (a multiple of 64), 0 = chosen by the planner
-                                  (batch-dependent in the same way as decode_split)                            */
+                                  (batch-dependent in the same way as decode_split). Capped at 1534 pages of
+                                  keys (rounded down to a multiple of 64), the page ids the prefill kernel stages
+                                  per item                                                                     */
     int32_t prefill_rows;      /* query rows (tokens x grouped heads) per prefill work group: 128 (4 waves, two
                                   work groups per CU), 256 (8 waves sharing each K/V tile, one per CU) or 0 =
                                   chosen by the planner (256 when the step has enough such tiles to fill the

@@ -401,6 +401,7 @@ namespace {
 constexpr int kPrefillRowsNarrow = 128;  // query rows (token x grouped head) of a 4-wave prefill work group
 constexpr int kPrefillRowsWide = 256;    // ... of an 8-wave one
 constexpr int kPrefillMaxPages = 1536;  // page ids of one prefill item the device kernel stages in LDS
+constexpr int kDecodeMaxPages = 1040;   // page ids of one decode split the device kernel stages in LDS
 constexpr int kNumCUs = 256;
 
 struct Item {
@@ -472,6 +473,9 @@ extern "C" cb_status cb_plan_attention(const int32_t *qsl, const int32_t *seq_le
         const int64_t per = ceil_div(dec_keys * Hkv, target_groups);
         S = int32_t(std::min<int64_t>(4096, std::max<int64_t>(256, ceil_div(per, 256) * 256)));
     }
+    // the decode kernel stages a split's page ids in LDS: at most kDecodeMaxPages - 2 pages of keys per split (a cap
+    // that depends on the page size only, so a caller-fixed split stays independent of the batch)
+    if (fast_decode) S = int32_t(std::min<int64_t>(S, int64_t(kDecodeMaxPages - 2) * P / 64 * 64));
     int32_t PS = sh->prefill_split;
     if (PS == 0) {
         // Split a tile's key range only as far as load balance needs: every split writes fp32 partial rows that the

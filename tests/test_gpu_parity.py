@@ -173,6 +173,10 @@ EDGE = {
                                        dtype="f32", Hq=4, Hkv=2, D=64, P=16),
     "many splits": dict(reqs=[(DECODING, 3000, 1), (DECODING, 70, 1), (PREFILLING, 1000, 300)],
                         decode_split=64, prefill_split=64),
+    # fixed splits far above the page ids the kernels stage per split: capped at 1038 (decode) and 1534 (prefill)
+    # pages, so the 9001-key decode row and the chunk's 12.5k-key tiles each take two splits of the largest size
+    "page 8 at the page-id staging limits": dict(reqs=[(DECODING, 9000, 1), (PREFILLING, 12500, 40)], P=8,
+                                                 decode_split=1 << 16, prefill_split=1 << 20),
 }
 
 

@@ -131,3 +131,22 @@ def test_plan_rejects_bad_input():
         cb.plan_attention([0, 1], [5], None, 8, 2, 128, 16, "bf16", -1, 100)  # split not a multiple of 64
     empty = cb.plan_attention([0], [], None, 8, 2, 128, 16, "bf16")
     assert empty.info.used == 0
+
+
+@pytest.mark.parametrize("P", [8, 16])
+def test_split_caps_at_page_staging_limits(P):
+    """A caller-fixed split is capped at the pages the kernels stage in LDS per split (decode 1038, prefill 1534;
+    rounded down to a multiple of 64 keys); the cap depends on the page size only, and the rows stay covered."""
+    qsl = np.array([0, 1, 41], np.int32)                       # one decode row, one 40-token chunk
+    seq = np.array([9001, 12540], np.int32) * (P // 8)
+    plan = cb.plan_attention(qsl, seq, None, 32, 8, 128, P, "bf16", -1, 1 << 16, 1 << 20)
+    dec_cap, pre_cap = 1038 * P // 64 * 64, 1534 * P // 64 * 64
+    assert plan.info.decode_split == dec_cap and plan.info.prefill_split == pre_cap
+    assert plan.counts()["decode"] == -(-int(seq[0]) // dec_cap) == 2
+    # each prefill tile (prefill_tokens tokens) reaches past the cap: two pieces per tile
+    n_tiles = -(-40 // plan.info.prefill_tokens)
+    assert plan.counts()["prefill"] == 2 * n_tiles
+    _cover_check(qsl, seq, None, plan, -1)
+    # below the caps a fixed split is used as given
+    small = cb.plan_attention(qsl, seq, None, 32, 8, 128, P, "bf16", -1, 1024, 2048)
+    assert small.info.decode_split == 1024 and small.info.prefill_split == 2048
