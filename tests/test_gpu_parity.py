@@ -177,6 +177,9 @@ EDGE = {
     # pages, so the 9001-key decode row and the chunk's 12.5k-key tiles each take two splits of the largest size
     "page 8 at the page-id staging limits": dict(reqs=[(DECODING, 9000, 1), (PREFILLING, 12500, 40)], P=8,
                                                  decode_split=1 << 16, prefill_split=1 << 20),
+    # four times the longest context of the benchmark's workloads: a 131001-key decode row (8188-entry block-table
+    # row) and a chunk at context 100000, with the planner's splits
+    "long context 131k": dict(reqs=[(DECODING, 131000, 1), (PREFILLING, 100000, 32)]),
 }
 
 
