@@ -180,6 +180,11 @@ EDGE = {
     # four times the longest context of the benchmark's workloads: a 131001-key decode row (8188-entry block-table
     # row) and a chunk at context 100000, with the planner's splits
     "long context 131k": dict(reqs=[(DECODING, 131000, 1), (PREFILLING, 100000, 32)]),
+    # the kernels' XCD mapping of (item, kv head) pairs: 16 kv heads (two per XCD) and 3 (no XCD grouping)
+    "16 kv heads": dict(reqs=[(DECODING, 2000, 1), (DECODING, 300, 1), (PREFILLING, 500, 200), (WAITING, 0, 90)],
+                        Hq=32, Hkv=16),
+    "3 kv heads": dict(reqs=[(DECODING, 2000, 1), (DECODING, 300, 1), (PREFILLING, 500, 200), (WAITING, 0, 90)],
+                       Hq=12, Hkv=3),
 }
 
 
