@@ -164,6 +164,8 @@ EDGE = {
     "group 16 (decode fast path limit)": dict(reqs=[(DECODING, 500, 1), (PREFILLING, 64, 20)], Hq=32, Hkv=2),
     "group 32 (decode via per-token kernel)": dict(reqs=[(DECODING, 500, 1), (PREFILLING, 64, 20)], Hq=32, Hkv=1),
     "MHA group 1": dict(reqs=[(DECODING, 333, 1), (WAITING, 0, 200)], Hq=4, Hkv=4),
+    "group 8 (16 or 32 tokens per prefill tile)": dict(reqs=[(DECODING, 700, 1), (PREFILLING, 300, 100),
+                                                              (WAITING, 0, 77)], Hq=16, Hkv=2),
     "bf16 page 4 (per-token kernel)": dict(reqs=[(DECODING, 77, 1), (PREFILLING, 10, 30)], P=4),
     "sliding window 0": dict(reqs=[(DECODING, 50, 1), (PREFILLING, 40, 33)], window_left=0, ring_len=8, budget=64),
     "sliding window 1": dict(reqs=[(DECODING, 50, 1), (PREFILLING, 40, 33)], window_left=1, ring_len=8, budget=64),
