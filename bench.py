@@ -364,6 +364,49 @@ def measure(index: int, steps: int, warmup: int, args, dist_steps: int, flush_st
     return res, w, step, pipe
 
 
+def measure_loop(index: int, steps: int, warmup: int) -> dict:
+    """A serving loop over the workload's requests: every step is scheduled from the request state the previous step
+    left (each decode's context grows by one key, requests take fresh pages as they cross page boundaries, chunks
+    advance), so consecutive steps differ in seq_lens, block tables and plans. The same loop, from the same start
+    state, runs twice: with eager launches, and replaying HIP graphs captured per padded shape. Wall clock per step,
+    the host's scheduling, planning, padding and request bookkeeping (the lifecycle in native code, in place)
+    included, as in a serving loop; the new rows' values are not rewritten between steps (timing only: the
+    serving-loop parity tests check the outputs)."""
+    import torch
+    from harness import build_step, pipeline_for
+    from synth import make_workload
+
+    w = make_workload(index)
+    step = build_step(w, threads=16)
+    res = {"workload": w.name, "index": index, "steps": steps, "warmup": warmup}
+    for mode in ("eager", "graph replay by padded shape"):
+        pipe = pipeline_for(w, step, graphs=mode != "eager")
+        toks = 0
+        for k in range(warmup + steps):
+            if k == warmup:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                captures0 = pipe.captures
+            views = pipe.prepare()
+            pipe.launch(views)
+            if k >= warmup:
+                toks += pipe.num_tokens
+            pipe.advance()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        r = {"ms_per_step": round(ms, 5), "value": round(toks / (ms * steps / 1e3), 1), "unit": "query tokens/s"}
+        if mode != "eager":
+            r.update({"captures_in_timed_steps": pipe.captures - captures0, "captures": pipe.captures,
+                      "replays": pipe.replays, "graphs_kept": len(pipe.graphs)})
+        res[mode] = r
+        log(f"[bench] serving loop, workload {index}, {mode}: {ms:.4f} ms/step")
+        del pipe
+        torch.cuda.synchronize()
+    del step
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -398,6 +441,9 @@ def main():
     ap.add_argument("--swap-pages", type=int, default=0,
                     help="also measure offloading N cache pages of the first layer to pinned host memory and back "
                          "(gather kernel, device-to-host copy, host-to-device copy, scatter kernel)")
+    ap.add_argument("--loop-workload", type=int, default=2, choices=[2, 3, 4, 5],
+                    help="workload of the serving-loop pass (eager launches against graph replay by padded shape)")
+    ap.add_argument("--loop-steps", type=int, default=64, help="timed steps of the serving-loop pass (0: no pass)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, run a plain device copy of this many MiB three times (untimed), the "
                          "known-size reference for scaling HBM byte counters")
@@ -448,6 +494,8 @@ def main():
         del st, pp
         torch.cuda.empty_cache()
 
+    loop = measure_loop(args.loop_workload, args.loop_steps, 16) if args.loop_steps else None
+
     base = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
@@ -463,7 +511,7 @@ def main():
         "step_us": head["step_us"], "kv_gb_per_s": head["kv_gb_per_s"], "kernel_us": head["kernel_us"],
         "roofline": head["roofline"], "roofline_prefill": head["roofline_prefill"],
         "flushed": head.get("flushed"), "concurrent_prefill_stream": head.get("concurrent_prefill_stream"),
-        "per_config": per_config, "cpu_baseline": base,
+        "per_config": per_config, "serving_loop": loop, "cpu_baseline": base,
     }
     if "graphs" in head:
         line["graphs"] = head["graphs"]

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 7
+#define CB_ABI_VERSION 8
 
 typedef int32_t cb_status;
 #define CB_OK 0
@@ -171,6 +171,34 @@ typedef struct cb_step {
  */
 cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const cb_sched_params *params,
                             const cb_layer_pool *layers, int32_t *out, int64_t out_capacity, cb_step *step);
+
+/*
+ * Request lifecycle after a step has run (Transformers "continuous batching architecture" page, section "请求生命周期":
+ * a waiting request is admitted and prefilled in chunks, then decodes one token per step), done in place on the
+ * arrays the next cb_build_metadata call reads, so that a serving loop's host half stays in native code.
+ * buf/step: the step's metadata as cb_build_metadata wrote it from these same reqs/params/layers. For every row r
+ * the step scheduled (request i = req_index[r]):
+ *   - the keys up to seq_len[r] are in the cache: num_pending drops by seq_len[r] - num_computed (this step's
+ *     tokens plus any prompt tokens reused from the prefix cache) and num_computed becomes seq_len[r];
+ *   - a request whose prompt is done decodes next (CB_DECODING, one pending token: the token this step produced),
+ *     otherwise it keeps prefilling (CB_PREFILLING);
+ *   - per layer type its pages become its block-table row: the first ceil(seq_len / page_size) entries, or its
+ *     whole ring. They are copied to page_store + (i * n_layers + l) * store_stride and reqs[i].pages[l] points
+ *     there (page_store: host int32 [n_reqs][n_layers][store_stride], caller-owned, must outlive every later use
+ *     of reqs);
+ *   - when the step shared prefixes (step->prefix_sharing), every prompt block the step completed (blocks
+ *     ctx / page_size .. min(seq_len / page_size, n_prompt_blocks) - 1) is registered in params->prefix_cache under
+ *     its hash (cb_pcache_commit), so that later requests can reuse it.
+ * Requests the step did not schedule are unchanged. Unless the step shared prefixes (its pages then came from the
+ * cache's allocator), each pool's free list moves past the pages the step took: layers[l].free_pages +=
+ * used_pages[l], layers[l].n_free -= used_pages[l] (the caller's array itself is not written).
+ * Everything is checked before anything changes: CB_E_INVAL (a row index out of range or repeated, a seq_len
+ * below the request's context, more used pages than a free list holds, a completed block's page not held or
+ * already registered) or CB_E_CAPACITY (a row needs more than store_stride pages) leave all arguments unchanged.
+ * Host only; allocates nothing the caller sees.
+ */
+cb_status cb_advance(cb_req *reqs, int32_t n_reqs, const cb_sched_params *params, cb_layer_pool *layers,
+                     const int32_t *buf, const cb_step *step, int32_t *page_store, int32_t store_stride);
 
 /*
  * Cache slots of key positions lo .. hi-1 of one request: out[i] = page * page_size + (p % page_size) for p = lo + i,

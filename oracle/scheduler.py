@@ -246,3 +246,49 @@ def build_metadata(requests, layers, max_batch_tokens, max_requests, page_size, 
         out["layers"].append({"block_table": table, "slot_mapping": slots,
                               "ring_len": np.full(N, R, dtype=np.int32), "used_pages": taken[l], "width": width})
     return out
+
+
+def advance(requests, schedule, free_pages, page_size, prefix_cache=None, prompt_hashes=None):
+    """The request lifecycle after a step has run (Transformers "continuous batching architecture" page, section
+    "请求生命周期"): a waiting request is admitted and prefilled chunk by chunk; once its whole prompt is in the
+    cache it decodes, one token per step.
+
+    Readings: after the step, request i = req_index[r] holds every key up to seq_lens[r], so its context becomes
+    seq_lens[r] and its pending prompt shrinks by the keys gained (this step's tokens plus any prompt blocks it
+    reused from the prefix cache); with nothing left it turns to decoding, with one pending token (the one just
+    produced). Its pages are what its block-table row addresses: ceil(seq_len / page_size) pages, or its whole ring.
+    The step's pages came off the front of each free list, unless the step shared prefixes: then they came from the
+    prefix cache, which registers (commit) each prompt block the step filled completely. Unscheduled requests keep
+    their state. Returns (requests, free_pages) as new lists; the input is not modified."""
+    import copy
+    P = page_size
+    out = [copy.copy(rq) for rq in requests]
+    for rq in out:
+        rq.pages = [np.asarray(p, dtype=np.int32).copy() for p in rq.pages]
+    shared = bool(schedule.get("prefix_sharing", False))
+    qsl, seqs = schedule["query_start_loc"], schedule["seq_lens"]
+    for r, i in enumerate(schedule["req_index"]):
+        rq = out[int(i)]
+        seq = int(seqs[r])
+        context = seq - int(qsl[r + 1] - qsl[r])
+        if shared and prefix_cache is not None and prompt_hashes is not None and prompt_hashes[int(i)] is not None:
+            hashes = prompt_hashes[int(i)]
+            row = schedule["layers"][0]["block_table"][r]
+            for blk in range(context // P, min(seq // P, len(hashes))):   # blocks this step completed
+                prefix_cache.commit(int(row[blk]), int(hashes[blk]))
+        gained = seq - rq.num_computed
+        rq.num_computed = seq
+        rq.num_pending = rq.num_pending - gained
+        if rq.num_pending > 0:
+            rq.state = PREFILLING
+        else:
+            rq.state, rq.num_pending = DECODING, 1
+        for l, lay in enumerate(schedule["layers"]):
+            ring = int(lay["ring_len"][r])
+            keep = ring if ring > 0 else _cdiv(seq, P)
+            rq.pages[l] = np.array(lay["block_table"][r][:keep], dtype=np.int32)
+    free = []
+    for l, lay in enumerate(schedule["layers"]):
+        taken = 0 if shared else int(lay["used_pages"])
+        free.append(np.asarray(free_pages[l], dtype=np.int32)[taken:].copy())
+    return out, free

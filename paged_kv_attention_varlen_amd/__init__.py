@@ -148,47 +148,75 @@ class Request:
     pages: list
 
 
+def _pack_schedule(schedule: dict):
+    """The step metadata of `schedule` (as build_metadata returns it) as a packed int32 buffer and its cb_step
+    header: the parts cb_advance reads (rows, seq_lens, req_index, block tables, used pages, prefix sharing)."""
+    N = int(schedule["num_reqs"])
+    parts = [_i32(schedule["query_start_loc"]), _i32(schedule["seq_lens"]), _i32(schedule["req_index"])]
+    hdr = _abi.cb_step()
+    hdr.num_reqs, hdr.num_tokens = N, int(schedule["num_tokens"])
+    hdr.prefix_sharing = int(bool(schedule.get("prefix_sharing", False)))
+    hdr.max_seq_len = int(schedule["seq_lens"].max()) if N else 0
+    at = 0
+    hdr.off_query_start_loc, at = at, at + N + 1
+    hdr.off_seq_lens, at = at, at + N
+    hdr.off_req_index, at = at, at + N
+    for l, lay in enumerate(schedule["layers"]):
+        bt = _i32(lay["block_table"]).reshape(-1)
+        hdr.table_width[l] = int(lay["width"])
+        hdr.used_pages[l] = int(lay["used_pages"])
+        hdr.off_block_table[l], at = at, at + bt.size
+        parts.append(bt)
+    return np.ascontiguousarray(np.concatenate(parts).astype(np.int32)), hdr
+
+
+def _store_stride(step, rings, page_size: int) -> int:
+    """Pages per request and layer that cb_advance may write after the step `step` (its longest row, or a ring)."""
+    return max([-(-int(step.max_seq_len) // page_size)] + [int(r) for r in rings] + [1])
+
+
+def _unmarshal_requests(requests, reqs, L):
+    """Request records from the marshalled cb_req array (page lists copied out of the library's view)."""
+    out = []
+    for i, rq in enumerate(requests):
+        r = reqs[i]
+        pages = [np.ctypeslib.as_array(r.pages[l], shape=(r.n_pages[l],)).copy() if r.n_pages[l] > 0
+                 else np.zeros(0, np.int32) for l in range(L)]
+        out.append(Request(int(rq.id), int(r.state), int(r.num_computed), int(r.num_pending), pages))
+    return out
+
+
 def advance(requests, schedule: dict, free_pages, ring_lens, page_size: int, prefix_cache=None,
             prompt_hashes=None):
-    """Request lifecycle after a step has run (Transformers "continuous batching architecture" page, section
-    "请求生命周期": a waiting request is admitted and prefilled in chunks, then decodes one token per step).
+    """Request lifecycle after a step has run (cb_advance; Transformers "continuous batching architecture" page,
+    section "请求生命周期": a waiting request is admitted and prefilled in chunks, then decodes one token per step).
 
-    schedule: the step's metadata as `build_metadata` returns it (query_start_loc, seq_lens, req_index and per layer
-    the block table and used_pages). Every scheduled request has now computed its keys up to its seq_len (its
-    q_len tokens, plus any prompt tokens it reused from the prefix cache): a request whose prompt is done decodes
-    next (one pending token: the one this step produced), otherwise it keeps prefilling; its pages are its
-    block-table row (ceil(seq_len / page_size) pages, or its whole ring). Pages the step took leave the front of
-    each free list (unless the prefix cache allocated them). With a prefix cache, every prompt block the step
-    completed is registered under its hash (prompt_hashes[i], chain hashes of request i's full prompt blocks), so
-    that later requests can reuse it (same page, section "前缀缓存": every completed block is content-hashed).
-    Requests the step did not schedule are unchanged. Returns (requests, free_pages) as new lists (Request records
-    in the input order)."""
-    qsl, seq, idx = schedule["query_start_loc"], schedule["seq_lens"], schedule["req_index"]
-    P = int(page_size)
-    out = [Request(int(r.id), int(r.state), int(r.num_computed), int(r.num_pending),
-                   [np.asarray(p, dtype=np.int32) for p in r.pages]) for r in requests]
-    for row in range(len(idx)):
-        i = int(idx[row])
-        rq = out[i]
-        q = int(qsl[row + 1] - qsl[row])
-        ctx = int(seq[row]) - q
-        if prefix_cache is not None and prompt_hashes is not None and prompt_hashes[i] is not None:
-            table = schedule["layers"][0]["block_table"][row]
-            for b in range(ctx // P, min(int(seq[row]) // P, len(prompt_hashes[i]))):
-                prefix_cache.commit(int(table[b]), int(prompt_hashes[i][b]))
-        rq.num_pending -= int(seq[row]) - rq.num_computed
-        rq.num_computed = int(seq[row])
-        if rq.num_pending <= 0:
-            rq.state, rq.num_pending = CB_DECODING, 1
-        else:
-            rq.state = CB_PREFILLING
-        for l, lay in enumerate(schedule["layers"]):
-            n = int(ring_lens[l]) if ring_lens[l] > 0 else -(-int(seq[row]) // page_size)
-            rq.pages[l] = np.array(lay["block_table"][row, :n], dtype=np.int32)
-    shared = schedule.get("prefix_sharing", False)
-    free = [np.asarray(f, dtype=np.int32)[0 if shared else int(lay["used_pages"]):].copy()
-            for f, lay in zip(free_pages, schedule["layers"])]
-    return out, free
+    schedule: the step's metadata as `build_metadata` returns it. Every scheduled request has now computed its keys
+    up to its seq_len (its q_len tokens, plus any prompt tokens it reused from the prefix cache): a request whose
+    prompt is done decodes next (one pending token: the one this step produced), otherwise it keeps prefilling; its
+    pages are its block-table row (ceil(seq_len / page_size) pages, or its whole ring). Pages the step took leave the
+    front of each free list, unless the step shared prefixes (the prefix cache allocated them); then every prompt
+    block the step completed is registered in `prefix_cache` under its hash (prompt_hashes[i], chain hashes of
+    request i's full prompt blocks), so that later requests can reuse it. Requests the step did not schedule are
+    unchanged. Returns (requests, free_pages) as new lists (Request records in the input order)."""
+    lib = _abi.load()
+    L = len(schedule["layers"])
+    n = len(requests)
+    keep = []
+    reqs = _marshal_requests(requests, L, prompt_hashes, keep)
+    buf, hdr = _pack_schedule(schedule)
+    pools = (_abi.cb_layer_pool * max(L, 1))()
+    free = [_i32(f) for f in free_pages]
+    for l in range(L):
+        pools[l] = _abi.cb_layer_pool(int(ring_lens[l]), -1, 0, free[l].size, _ptr(free[l]))
+    params = _abi.cb_sched_params(1, 1, int(page_size), 0, L, CB_POLICY_FIFO, 0.0,
+                                  prefix_cache._h if prefix_cache is not None else None)
+    stride = _store_stride(hdr, ring_lens, page_size)
+    store = np.zeros(max(n, 1) * L * stride, dtype=np.int32)
+    st = lib.cb_advance(reqs, n, C.byref(params), pools, _ptr(buf), C.byref(hdr), _ptr(store), stride)
+    if st != CB_OK:
+        raise CbError(st, "cb_advance")
+    return _unmarshal_requests(requests, reqs, L), [f[f.size - pools[l].n_free:].copy() for l, f in enumerate(free)]
 
 
 def schedule_arrays(buf: np.ndarray, step, n_layers: int) -> dict:
@@ -242,8 +270,9 @@ class Scheduler:
         keep = []
         n = len(requests)
         self.n = n
-        self.requests = list(requests)
-        self.free_pages = [np.asarray(f, dtype=np.int32) for f in free_pages]
+        self._requests = list(requests)
+        self._free_pages = [np.asarray(f, dtype=np.int32) for f in free_pages]
+        self._stale = False
         reqs = _marshal_requests(requests, L, self.prompt_hashes, keep)
         if pool_pages is None:
             pool_pages = [self.pools[l].pool_pages for l in range(L)]
@@ -253,10 +282,67 @@ class Scheduler:
             keep.append(f)
             pools[l] = _abi.cb_layer_pool(self.rings[l], self.windows[l], int(pool_pages[l]), f.size, _ptr(f))
         self.reqs, self.pools, self._keep = reqs, pools, keep
+        # page lists written by advance_step: [n][L][stride], grown (and the requests' pages moved) when a step needs
+        # more pages per request than it holds
+        self._store_stride = max([1] + [int(reqs[i].n_pages[l]) for i in range(n) for l in range(L)])
+        self._store = np.zeros(max(n, 1) * L * self._store_stride, dtype=np.int32)
+
+    @property
+    def requests(self):
+        """The request records (arrival order) as the scheduler's state holds them now."""
+        self._sync()
+        return self._requests
+
+    @property
+    def free_pages(self):
+        """Each layer type's free list (allocation order) as the scheduler's state holds it now."""
+        self._sync()
+        return self._free_pages
+
+    def _sync(self) -> None:
+        if not self._stale:
+            return
+        self._requests = _unmarshal_requests(self._requests, self.reqs, self.L)
+        self._free_pages = [np.ctypeslib.as_array(p.free_pages, shape=(p.n_free,)).copy() if p.n_free > 0
+                            else np.zeros(0, np.int32) for p in self.pools[:self.L]]
+        self._stale = False
+
+    def _grow_store(self, stride: int) -> None:
+        """A page store of `stride` pages per request and layer; requests whose pages live in the old one move."""
+        L = self.L
+        old = self._store
+        new = np.zeros(max(self.n, 1) * L * stride, dtype=np.int32)
+        base, end = old.ctypes.data, old.ctypes.data + old.nbytes
+        for i in range(self.n):
+            r = self.reqs[i]
+            for l in range(L):
+                addr = C.cast(r.pages[l], C.c_void_p).value or 0
+                if base <= addr < end:
+                    k = r.n_pages[l]
+                    src = (addr - base) // 4
+                    dst = (i * L + l) * stride
+                    new[dst:dst + k] = old[src:src + k]
+                    r.pages[l] = C.cast(C.c_void_p(new.ctypes.data + 4 * dst), _abi.i32p)
+        self._keep.append(old)     # kept alive until the next set_state
+        self._store, self._store_stride = new, stride
+
+    def advance_step(self, step: _abi.cb_step, buf: np.ndarray) -> None:
+        """After the step that build_into scheduled into `buf` (header `step`) has run: the request lifecycle
+        (cb_advance) on the scheduler's marshalled requests and free lists, in place, with no per-request Python
+        work; the `requests` / `free_pages` views catch up when read."""
+        need = _store_stride(step, self.rings, self.page_size)
+        if need > self._store_stride:
+            self._grow_store(max(need, 2 * self._store_stride))
+        st = self._lib.cb_advance(self.reqs, self.n, C.byref(self.params), self.pools, buf.ctypes.data_as(_abi.i32p),
+                                  C.byref(step), _ptr(self._store), self._store_stride)
+        if st != CB_OK:
+            raise CbError(st, "cb_advance")
+        self._stale = True
 
     def advance(self, schedule: dict) -> None:
-        """After the step `schedule` has run: move every request along its lifecycle (`advance`) and drop the pages
-        the step took from the free lists."""
+        """After the step `schedule` (numpy form, e.g. schedule_arrays) has run: move every request along its
+        lifecycle (`advance`) and drop the pages the step took from the free lists. advance_step does the same on
+        the raw metadata buffer without leaving native code."""
         reqs, free = advance(self.requests, schedule, self.free_pages, self.rings, self.page_size, self.prefix_cache,
                              self.prompt_hashes)
         self.set_state(reqs, free)

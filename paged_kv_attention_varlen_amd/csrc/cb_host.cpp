@@ -338,6 +338,98 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
     return (N == 0 && blocked) ? CB_E_NOSPACE : CB_OK;
 }
 
+// ------------------------------------------------------------------------------------------ request lifecycle
+
+extern "C" cb_status cb_advance(cb_req *reqs, int32_t n_reqs, const cb_sched_params *params, cb_layer_pool *layers,
+                                const int32_t *buf, const cb_step *step, int32_t *page_store, int32_t store_stride) {
+    if (!params || !layers || !buf || !step || n_reqs < 0 || (n_reqs > 0 && !reqs) || store_stride < 0)
+        return CB_E_INVAL;
+    const int32_t P = params->page_size;
+    const int32_t L = params->n_layers;
+    const int32_t N = step->num_reqs;
+    if (P < 1 || L < 1 || L > CB_MAX_LAYERS || N < 0 || N > n_reqs) return CB_E_INVAL;
+    if (N > 0 && !page_store) return CB_E_INVAL;
+    cb_prefix_cache *pc = step->prefix_sharing ? params->prefix_cache : nullptr;
+    if (step->prefix_sharing && !pc) return CB_E_INVAL;
+    const int32_t *qsl = buf + step->off_query_start_loc;
+    const int32_t *seq = buf + step->off_seq_lens;
+    const int32_t *idx = buf + step->off_req_index;
+    auto pages_after = [&](int l, int32_t s) -> int64_t {
+        return layers[l].ring_len > 0 ? layers[l].ring_len : ceil_div(s, P);
+    };
+    // blocks [first, end) of row r's prompt that this step completed (registered when the step shared prefixes)
+    auto completed = [&](int32_t r, int32_t &first, int32_t &end) {
+        const cb_req &rq = reqs[idx[r]];
+        first = (seq[r] - (qsl[r + 1] - qsl[r])) / P;
+        end = std::min(seq[r] / P, rq.prompt_hashes ? rq.n_prompt_blocks : 0);
+    };
+
+    // everything is checked before anything changes
+    if (qsl[0] != 0) return CB_E_INVAL;
+    std::vector<uint8_t> seen(size_t(n_reqs), 0);
+    for (int32_t r = 0; r < N; ++r) {
+        const int32_t i = idx[r];
+        if (i < 0 || i >= n_reqs || seen[size_t(i)]) return CB_E_INVAL;
+        seen[size_t(i)] = 1;
+        const cb_req &rq = reqs[i];
+        const int32_t q = qsl[r + 1] - qsl[r];
+        const int32_t ctx = seq[r] - q;
+        if (q < 0 || ctx < rq.num_computed) return CB_E_INVAL;
+        for (int l = 0; l < L; ++l) {
+            const int64_t n = pages_after(l, seq[r]);
+            if (n > step->table_width[l]) return CB_E_INVAL;
+            if (n > store_stride) return CB_E_CAPACITY;
+        }
+        if (pc) {
+            int32_t b0, b1;
+            completed(r, b0, b1);
+            const int32_t *row = buf + step->off_block_table[0] + int64_t(r) * step->table_width[0];
+            for (int32_t b = b0; b < b1; ++b) {
+                int32_t refs = 0, registered = 0;
+                uint64_t h = 0;
+                if (cb_pcache_page_info(pc, row[b], &refs, &registered, &h) != CB_OK || refs < 1 || registered)
+                    return CB_E_INVAL;
+            }
+        }
+    }
+    if (!step->prefix_sharing)
+        for (int l = 0; l < L; ++l)
+            if (step->used_pages[l] < 0 || step->used_pages[l] > layers[l].n_free) return CB_E_INVAL;
+
+    for (int32_t r = 0; r < N; ++r) {
+        const int32_t i = idx[r];
+        cb_req &rq = reqs[i];
+        if (pc) {
+            int32_t b0, b1;
+            completed(r, b0, b1);
+            const int32_t *row = buf + step->off_block_table[0] + int64_t(r) * step->table_width[0];
+            for (int32_t b = b0; b < b1; ++b) cb_pcache_commit(pc, row[b], rq.prompt_hashes[b]);
+        }
+        // the keys up to seq_len are in the cache now: this step's tokens and any prompt tokens reused from the cache
+        rq.num_pending -= seq[r] - rq.num_computed;
+        rq.num_computed = seq[r];
+        if (rq.num_pending <= 0) {
+            rq.state = CB_DECODING;   // the prompt is done: the token this step produced is fed next
+            rq.num_pending = 1;
+        } else {
+            rq.state = CB_PREFILLING;
+        }
+        for (int l = 0; l < L; ++l) {
+            const int64_t n = pages_after(l, seq[r]);
+            int32_t *dst = page_store + (int64_t(i) * L + l) * store_stride;
+            std::memcpy(dst, buf + step->off_block_table[l] + int64_t(r) * step->table_width[l], size_t(n) * 4);
+            rq.pages[l] = dst;
+            rq.n_pages[l] = int32_t(n);
+        }
+    }
+    if (!step->prefix_sharing)
+        for (int l = 0; l < L; ++l) {
+            layers[l].free_pages += step->used_pages[l];
+            layers[l].n_free -= step->used_pages[l];
+        }
+    return CB_OK;
+}
+
 extern "C" cb_status cb_slot_mapping(const int32_t *pages, int32_t n_pages, int32_t ring_len, int32_t page_size,
                                      int32_t lo, int32_t hi, int32_t *out) {
     if (page_size < 1 || n_pages < 0 || ring_len < 0 || lo < 0 || hi < lo) return CB_E_INVAL;

@@ -451,6 +451,12 @@ class StepPipeline:
         """One full step: prepare() then launch()."""
         self.launch(self.prepare(), events)
 
+    def advance(self) -> None:
+        """The request lifecycle after the last prepared step (Scheduler.advance_step, in native code, on the pinned
+        metadata that step was scheduled into). A serving loop calls it once per step, after launch() and before
+        the next prepare(); without it every step repeats the same schedule."""
+        self.sched.advance_step(self.last_header, self.host[self.cur].numpy())
+
     def launch(self, views, events=None):
         """The device half of a prepared step. A caller that writes the step's new Q/K/V rows after seeing its
         schedule (keep_schedule) does so between prepare() and launch(), in stream order on the compute stream.

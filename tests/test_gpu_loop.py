@@ -1,7 +1,8 @@
 """GPU parity of a serving loop: steps whose schedules differ from one step to the next.
 
 The package's pipeline schedules every step from the current request state (cb_build_metadata), the harness writes
-the step's new Q/K/V rows, the kernels run, and the request lifecycle moves on (advance): decodes grow their
+the step's new Q/K/V rows, the kernels run, and the request lifecycle moves on (cb_advance, in place on the
+scheduler's state): decodes grow their
 context by one key per step, prefill chunks continue, a waiting prompt is admitted and prefilled in chunks, then
 decodes. Every step is checked against the oracle run on the same request state, in three modes: the metadata copy
 on its own stream (eager launches), graph replay by padded shape, and per-phase launches between timing events.
@@ -88,7 +89,7 @@ def _loop(torch, w, steps, mode, rows, sample=None, seed=0):
                 assert events[l][0].elapsed_time(events[l][1]) >= 0.0
         print(f"[gpu] {mode} step {k}: T={T} N={s['num_reqs']} decodes={s['num_decodes']} key={pipe.key}",
               flush=True)
-        pipe.sched.advance(s)
+        pipe.advance()
     return pipe, shapes
 
 
@@ -134,5 +135,5 @@ def test_graph_cache_stays_bounded(torch_gpu):
         pipe.launch(views)
         torch_gpu.cuda.synchronize()
         assert len(pipe.graphs) <= 2
-        pipe.sched.advance(pipe.last_schedule)
+        pipe.advance()
     assert pipe.captures > 2

@@ -466,8 +466,7 @@ def test_prefix_sharing_step(torch_gpu):
     reqs = [cb.Request(0, WAITING, 0, 100, [np.zeros(0, np.int32)])]
     s1, hs = schedule(reqs)
     reqs, _ = cb.advance(reqs, s1, [np.zeros(0, np.int32)], [0], P, pc, hs)
-    cb.advance([cb.Request(0, WAITING, 0, 100, [np.zeros(0, np.int32)])], s1, [np.zeros(0, np.int32)], [0], P, oc,
-               hs)
+    OS.advance([cb.Request(0, WAITING, 0, 100, [np.zeros(0, np.int32)])], s1, [np.zeros(0, np.int32)], P, oc, hs)
     pages_a = reqs[0].pages[0]
     assert pc.stats()[2] == 6                                            # A's six full blocks are registered
     reqs.append(cb.Request(1, WAITING, 0, len(prompt_b), [np.zeros(0, np.int32)]))

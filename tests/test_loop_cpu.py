@@ -76,3 +76,131 @@ def test_multi_step_metadata_equals_the_oracle_scheduler():
             reqs, free = cb.advance(wk.requests, got, free, rings, w.page_size)
         assert {DECODING, PREFILLING, WAITING} <= states
         assert all(r.state == DECODING for r in reqs)
+
+
+def _random_loop(seed, steps=24):
+    """A random serving loop: one full layer type, or a full and a sliding one (ring); FIFO or PrefillFirst; requests
+    arrive over time with random prompt lengths. Yields the layer pool dicts, budget, page size and policy, and per
+    step the new arrivals."""
+    rng = np.random.default_rng(seed)
+    P = int(rng.choice([2, 4, 8, 16]))
+    budget = int(rng.integers(P, 8 * P))
+    hybrid = bool(rng.integers(0, 2))
+    policy = "prefill_first" if rng.integers(0, 3) == 0 else "fifo"
+    layers = []
+    for l in range(2 if hybrid else 1):
+        n_pages = int(rng.integers(60, 400))
+        free = (rng.permutation(np.arange(2, n_pages)) if rng.integers(0, 2) else np.arange(2, n_pages))
+        if l == 1:
+            window = int(rng.integers(1, 6 * P))
+            ring = (window + budget + P - 2) // P + 1 + int(rng.integers(0, 3))
+            layers.append({"ring_len": ring, "window_left": window, "pool_pages": n_pages - 2,
+                           "free_pages": free.astype(np.int32)})
+        else:
+            layers.append({"ring_len": 0, "window_left": -1, "pool_pages": n_pages - 2,
+                           "free_pages": free.astype(np.int32)})
+    arrivals = [[int(rng.integers(1, 5 * P)) for _ in range(int(rng.integers(0, 3)))] for _ in range(steps)]
+    return layers, budget, P, policy, arrivals
+
+
+def _same_requests(a, b):
+    assert len(a) == len(b)
+    for x, y in zip(a, b):
+        assert (x.id, x.state, x.num_computed, x.num_pending) == (y.id, y.state, y.num_computed, y.num_pending)
+        assert len(x.pages) == len(y.pages)
+        for p, q in zip(x.pages, y.pages):
+            assert np.array_equal(np.asarray(p), np.asarray(q))
+
+
+import pytest  # noqa: E402
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_native_lifecycle_equals_the_oracle_on_random_loops(seed):
+    """cb_advance (through the functional advance, and in place through Scheduler.advance_step on the raw metadata
+    buffer) equals the oracle's lifecycle step by step: request states, contexts, pending tokens, pages and free
+    lists, over random serving loops with arrivals, chunked prompts, decodes, rings and both policies."""
+    layers, budget, P, policy, arrivals = _random_loop(seed)
+    L = len(layers)
+    reqs_o, free_o = [], [lay["free_pages"].copy() for lay in layers]
+    reqs_f, free_f = [], [lay["free_pages"].copy() for lay in layers]
+    sched = cb.Scheduler([], layers, budget, 16, P, 0.0, 0, policy=policy)
+    buf = np.zeros(1 << 16, dtype=np.int32)
+    next_id = 0
+    ran = 0
+    for k, new in enumerate(arrivals):
+        for n in new:
+            for lst in (reqs_o, reqs_f):
+                lst.append(cb.Request(next_id, WAITING, 0, n, [np.zeros(0, np.int32) for _ in range(L)]))
+            next_id += 1
+        if new:
+            sched.set_state(sched.requests + [cb.Request(r.id, r.state, r.num_computed, r.num_pending,
+                                                         [p.copy() for p in r.pages]) for r in reqs_f[-len(new):]],
+                            sched.free_pages)
+        pools_o = [dict(lay, free_pages=f) for lay, f in zip(layers, free_o)]
+        want = OS.build_metadata(reqs_o, pools_o, budget, 16, P, 0.0, 0, policy=policy)
+        if want["status"] != "ok":
+            break
+        got = cb.build_metadata(reqs_f, [dict(lay, free_pages=f) for lay, f in zip(layers, free_f)], budget, 16, P,
+                                0.0, 0, policy=policy)
+        hdr = sched.build_into(buf)
+        assert np.array_equal(got["seq_lens"], want["seq_lens"]) and hdr.num_reqs == want["num_reqs"]
+        reqs_o, free_o = OS.advance(reqs_o, want, free_o, P)
+        reqs_f, free_f = cb.advance(reqs_f, got, free_f, [lay["ring_len"] for lay in layers], P)
+        sched.advance_step(hdr, buf)
+        ran += 1
+        _same_requests(reqs_f, reqs_o)
+        _same_requests(sched.requests, reqs_o)
+        for l in range(L):
+            assert np.array_equal(free_f[l], free_o[l]) and np.array_equal(sched.free_pages[l], free_o[l]), (k, l)
+    assert ran >= 4
+
+
+def test_advance_step_grows_its_page_store():
+    """A decode loop long enough that the requests' page lists outgrow the scheduler's page store: the store grows,
+    the pages move with it, and every step still equals the oracle's lifecycle."""
+    P = 2
+    layers = [{"ring_len": 0, "window_left": -1, "pool_pages": 300, "free_pages": np.arange(2, 302, dtype=np.int32)}]
+    reqs = [cb.Request(i, DECODING, 3, 1, [np.array([2 * i + 2, 2 * i + 3], np.int32)]) for i in range(3)]
+    free = [np.arange(8, 302, dtype=np.int32)]
+    sched = cb.Scheduler(reqs, [dict(layers[0], free_pages=free[0])], 64, 8, P)
+    stride0 = sched._store_stride
+    buf = np.zeros(4096, dtype=np.int32)
+    for k in range(40):
+        want = OS.build_metadata(reqs, [dict(layers[0], free_pages=free[0])], 64, 8, P)
+        hdr = sched.build_into(buf)
+        sched.advance_step(hdr, buf)
+        reqs, free = OS.advance(reqs, want, free, P)
+        _same_requests(sched.requests, reqs)
+        assert np.array_equal(sched.free_pages[0], free[0])
+    assert sched._store_stride > stride0
+
+
+def test_cb_advance_checks_before_changing_anything():
+    """A store too small for the step's rows (CB_E_CAPACITY), or a row index out of range (CB_E_INVAL): the call
+    fails and leaves the requests and free lists as they were."""
+    import ctypes as C
+    from paged_kv_attention_varlen_amd import _abi
+    P = 4
+    layers = [{"ring_len": 0, "window_left": -1, "pool_pages": 20, "free_pages": np.arange(2, 22, dtype=np.int32)}]
+    sched = cb.Scheduler([cb.Request(0, WAITING, 0, 10, [np.zeros(0, np.int32)])], layers, 16, 4, P)
+    buf = np.zeros(1024, dtype=np.int32)
+    hdr = sched.build_into(buf)
+    lib = _abi.load()
+    store = np.zeros(2, dtype=np.int32)
+    st = lib.cb_advance(sched.reqs, 1, C.byref(sched.params), sched.pools, buf.ctypes.data_as(_abi.i32p),
+                        C.byref(hdr), store.ctypes.data_as(_abi.i32p), 2)     # the row needs 3 pages
+    assert st == cb.CB_E_CAPACITY
+    assert sched.reqs[0].num_computed == 0 and sched.reqs[0].state == WAITING and sched.pools[0].n_free == 20
+    bad = buf.copy()
+    bad[hdr.off_req_index] = 5
+    store = np.zeros(16, dtype=np.int32)
+    st = lib.cb_advance(sched.reqs, 1, C.byref(sched.params), sched.pools, bad.ctypes.data_as(_abi.i32p),
+                        C.byref(hdr), store.ctypes.data_as(_abi.i32p), 4)
+    assert st == 1   # CB_E_INVAL
+    assert sched.reqs[0].num_computed == 0 and sched.pools[0].n_free == 20
+    sched.advance_step(hdr, buf)
+    r = sched.requests[0]
+    assert (r.state, r.num_computed, r.num_pending) == (PREFILLING, 10 if hdr.num_tokens == 10 else hdr.num_tokens,
+                                                        10 - hdr.num_tokens) or r.state == DECODING
+    assert sched.free_pages[0].size == 20 - hdr.used_pages[0]

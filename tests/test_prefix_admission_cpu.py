@@ -162,7 +162,7 @@ def test_library_matches_oracle_on_random_shared_prefix_loops(seed):
         assert sc["layers"][0]["used_pages"] == so["layers"][0]["used_pages"]
         matched_any |= bool(np.any(so["matched_tokens"] > 0))
         reqs_c, _ = cb.advance(reqs_c, sc, [np.zeros(0, np.int32)], [0], P, cc, hashes)
-        reqs_o, _ = cb.advance(reqs_o, so, [np.zeros(0, np.int32)], [0], P, co, hashes)
+        reqs_o, _ = S.advance(reqs_o, so, [np.zeros(0, np.int32)], P, co, hashes)
         assert _cache_state(cc, n_pages, True) == _cache_state(co, n_pages, False), (seed, step)
         # a decoding request finishes now and then: its pages go back (shared ones stay with their other holders)
         done = [k for k, r in enumerate(reqs_c) if r.state == DEC and rng.random() < 0.3]
