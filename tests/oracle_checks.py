@@ -526,6 +526,57 @@ def check_four_slot_timeline():
     assert sum(steps.values()) == g["total_tokens"]
 
 
+def check_request_lifecycle():
+    """The lifecycle after each step (Transformers page, section "请求生命周期"), hand-worked from its rules.
+    A 10-token prompt under a 4-token budget with 4-key pages prefills in chunks of 4, 4 and 2, then decodes one
+    token per step: (tokens, seq_len) per step (4, 4), (4, 8), (2, 10), (1, 11), (1, 12). After the fifth step it
+    decodes with context 12 and one pending token and owns ceil(12 / 4) = 3 pages, the first three of the free list
+    (2, 3, 4), whose front is then page 5. A sliding layer's request owns its whole ring from admission on. With
+    prefix sharing, a step registers exactly the prompt blocks it completed: a 10-token prompt with 4-key pages has
+    two full blocks, filled by the first two chunks of 4."""
+    P = 4
+    free = [np.arange(2, 22, dtype=np.int32)]
+    reqs = [Request(7, WAITING, 0, 10, [np.zeros(0, np.int32)])]
+    seen = []
+    for _ in range(5):
+        s = S.build_metadata(reqs, [_layer(0, -1, 20, free[0])], 4, 8, P)
+        seen.append((int(s["num_tokens"]), int(s["seq_lens"][0])))
+        reqs, free = S.advance(reqs, s, free, P)
+    assert seen == [(4, 4), (4, 8), (2, 10), (1, 11), (1, 12)], seen
+    r = reqs[0]
+    assert (r.state, r.num_computed, r.num_pending) == (DECODING, 12, 1)
+    assert r.pages[0].tolist() == [2, 3, 4] and int(free[0][0]) == 5
+    # a request the step leaves out keeps everything
+    idle = Request(8, WAITING, 0, 50, [np.zeros(0, np.int32)])
+    s = S.build_metadata([r, idle], [_layer(0, -1, 20, free[0])], 1, 8, P)
+    out, free2 = S.advance([r, idle], s, free, P)
+    assert (out[1].state, out[1].num_computed, out[1].num_pending) == (WAITING, 0, 50)
+    assert (out[0].num_computed, out[0].state, out[0].pages[0].tolist()) == (13, DECODING, [2, 3, 4, 5])
+    assert free2[0].tolist() == free[0][1:].tolist()
+    # ring layer: window 3, ring of 4 pages taken at admission; the pages stay the ring as the request grows
+    ring_free = [np.arange(30, 40, dtype=np.int32)]
+    q = [Request(1, WAITING, 0, 6, [np.zeros(0, np.int32)])]
+    for k in range(3):
+        s = S.build_metadata(q, [_layer(4, 3, 10, ring_free[0])], 4, 8, P)
+        q, ring_free = S.advance(q, s, ring_free, P)
+        assert q[0].pages[0].tolist() == [30, 31, 32, 33]
+    assert (q[0].num_computed, q[0].state) == (7, DECODING) and ring_free[0].tolist() == list(range(34, 40))
+    # prefix sharing: blocks 0 and 1 of the prompt are registered by the steps that complete them, block 2 never
+    from oracle.prefix_cache import PrefixCache, block_hashes
+    prompt = np.arange(100, 110, dtype=np.int32)
+    hashes = [block_hashes(prompt, P)]
+    cache = PrefixCache(20, list(range(2, 20)))
+    q = [Request(3, WAITING, 0, 10, [np.zeros(0, np.int32)])]
+    registered = []
+    for k in range(3):
+        s = S.build_metadata(q, [_layer(0, -1, 18, np.zeros(0, np.int32))], 4, 8, P, prefix_cache=cache,
+                             prompt_hashes=hashes)
+        q, _ = S.advance(q, s, [np.zeros(0, np.int32)], P, cache, hashes)
+        registered.append(sorted(cache.index.values()))
+    pages = q[0].pages[0].tolist()
+    assert registered == [[pages[0]], [pages[0], pages[1]], [pages[0], pages[1]]], (registered, pages)
+
+
 ALL_CHECKS = [
     check_worked_example_metadata, check_worked_example_address, check_explicit_mask,
     check_single_key_returns_value, check_equal_scores_give_mean, check_hand_solved_two_keys,
@@ -534,4 +585,5 @@ ALL_CHECKS = [
     check_batch_invariance, check_workload_paged_equals_definition, check_fifo_fill_of_workloads,
     check_padding_pages_never_allocated, check_admission_all_or_nothing, check_stall_nospace_margin_cap,
     check_prefill_first_order, check_swap_roundtrip_preserves_attention, check_four_slot_timeline,
+    check_request_lifecycle,
 ]

@@ -42,6 +42,29 @@ def _append_k_into_v(k_cache, v_cache, k_new, v_new, slot_mapping, page_size):
         v_cache[slot // page_size, slot % page_size] = k_new[t]
 
 
+_real_advance = S.advance
+
+
+def _advance_keeps_old_pages(requests, schedule, free_pages, page_size, *a, **k):
+    out, free = _real_advance(requests, schedule, free_pages, page_size, *a, **k)
+    for new, old in zip(out, requests):
+        new.pages = [np.asarray(p, dtype=np.int32).copy() for p in old.pages]
+    return out, free
+
+
+def _advance_free_list_unmoved(requests, schedule, free_pages, page_size, *a, **k):
+    out, _ = _real_advance(requests, schedule, free_pages, page_size, *a, **k)
+    return out, [np.asarray(f, dtype=np.int32).copy() for f in free_pages]
+
+
+def _advance_never_decodes(requests, schedule, free_pages, page_size, *a, **k):
+    out, free = _real_advance(requests, schedule, free_pages, page_size, *a, **k)
+    for new, old in zip(out, requests):
+        if new.state == S.DECODING and old.state != S.DECODING:
+            new.state = S.PREFILLING
+    return out, free
+
+
 MUTANTS = {
     "causal bound excludes the query itself": (A, "visible_range", _excl_self),
     "sliding window one key short": (A, "visible_range", _window_short),
@@ -53,6 +76,9 @@ MUTANTS = {
     "append writes K into V": (A, "kv_append", _append_k_into_v),
     "page counts rounded down": (S, "_cdiv", lambda a, b: a // b),
     "ring size never checked": (S, "ring_is_large_enough", lambda *a: True),
+    "lifecycle keeps the old pages": (S, "advance", _advance_keeps_old_pages),
+    "lifecycle leaves the free list unmoved": (S, "advance", _advance_free_list_unmoved),
+    "finished prompt never turns to decoding": (S, "advance", _advance_never_decodes),
 }
 
 
