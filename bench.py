@@ -494,7 +494,15 @@ def main():
         del st, pp
         torch.cuda.empty_cache()
 
-    loop = measure_loop(args.loop_workload, args.loop_steps, 16) if args.loop_steps else None
+    loop = None
+    if args.loop_steps:
+        try:
+            loop = measure_loop(args.loop_workload, args.loop_steps, 16)
+        except Exception as e:  # noqa: BLE001 - an extra pass must not cost the benchmark its line
+            log(f"[bench] serving loop failed: {e!r}")
+            loop = {"error": repr(e)}
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
 
     base = None
     if not args.no_cpu_baseline:
