@@ -194,6 +194,7 @@ class StepPipeline:
         self.key = None
         self.last_header = None    # cb_step header of the last prepared step
         self.last_plans = None     # its per-layer plan headers
+        self._advanced = 0         # the step count (self.k) at the last advance(): at most one per prepared step
         self.keep_schedule = False  # True: prepare() also keeps the step's metadata as numpy arrays (last_schedule)
         self.last_schedule = None
 
@@ -455,7 +456,10 @@ class StepPipeline:
         """The request lifecycle after the last prepared step (Scheduler.advance_step, in native code, on the pinned
         metadata that step was scheduled into). A serving loop calls it once per step, after launch() and before
         the next prepare(); without it every step repeats the same schedule."""
+        if self._advanced == self.k:
+            raise RuntimeError("advance() was already called for this step; prepare() the next step first")
         self.sched.advance_step(self.last_header, self.host[self.cur].numpy())
+        self._advanced = self.k
 
     def launch(self, views, events=None):
         """The device half of a prepared step. A caller that writes the step's new Q/K/V rows after seeing its
