@@ -16,6 +16,8 @@ Rules followed (Transformers "continuous batching architecture" page, sections "
   gives each request a fixed ring of `ring_len` pages at admission.
 * Metadata: query_start_loc [N+1] (exclusive prefix sum of the query lengths plus the total), seq_lens [N]
   (context + this step's tokens), block_table [N, width] padded with the padding page, slot_mapping [T].
+* After a step (`advance`, same page, section "请求生命周期"): each scheduled request's context is its seq_len, a
+  finished prompt turns to decoding, its pages are its block-table row, the free lists lose the step's pages.
 """
 from __future__ import annotations
 
