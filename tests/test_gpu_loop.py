@@ -139,14 +139,13 @@ def test_graph_cache_stays_bounded(torch_gpu):
     assert pipe.captures > 2
 
 
-@pytest.mark.parametrize("mode", ["copy stream", "graph replay"])
-def test_hybrid_pair_full_size_loop(torch_gpu, mode):
-    """The hybrid layer pair at full size (8192-token budget, full and sliding layers) as a three-step serving loop:
-    the native lifecycle moves the 128 decodes, the continuing chunks and the new prompt on between steps, and each
-    step's plans (the largest of the workloads) replace the last. Per step and layer: the longest decode row and 24
-    random rows against the oracle on the same request state, 48 of the pages the append touched bit for bit, and
-    every output row finite."""
+def test_hybrid_pair_full_size_loop(torch_gpu):
+    """The hybrid layer pair at full size (8192-token budget, full and sliding layers) as a three-step serving loop
+    replaying graphs by padded shape (eager loops run at full size for the decode-only step and at reduced size for
+    the layer pair above): the native lifecycle moves the 128 decodes, the continuing chunks and the new prompt on
+    between steps, and each step's plans (the largest of the workloads) replace the last. Per step and layer: the
+    longest decode row and 24 random rows against the oracle on the same request state, 48 of the pages the append
+    touched bit for bit, and every output row finite."""
     w = make_workload(5)
-    pipe, shapes = _loop(torch_gpu, w, 3, mode, rows=w.max_batch_tokens, sample=24, seed=55)
-    if mode == "graph replay":
-        assert pipe.replays == 3 and pipe.captures == len(shapes)
+    pipe, shapes = _loop(torch_gpu, w, 3, "graph replay", rows=w.max_batch_tokens, sample=24, seed=55)
+    assert pipe.replays == 3 and pipe.captures == len(shapes)
