@@ -280,6 +280,21 @@ cb_status cb_plan_attention(const int32_t *query_start_loc, const int32_t *seq_l
                             int32_t num_reqs, const cb_attn_shape *shape, int32_t *out, int64_t out_capacity,
                             cb_plan *plan);
 
+/*
+ * Schedule one step and plan every layer type of it, in one call, into one caller buffer: cb_build_metadata into
+ * out[0 .. meta_capacity), then cb_plan_attention of layer l (shape shapes[l]; its ring lengths from the step's
+ * metadata for a sliding layer) on the rows the step scheduled, into out[meta_capacity + plan_offsets[l] ..), the
+ * plans packed back to back within out_capacity. For serving loops that prepare a step per forward pass: one call
+ * instead of 1 + n_layers, with the plans placed where one copy to the device takes them with the metadata.
+ * shapes: [params->n_layers]; plans, plan_offsets: [params->n_layers] (caller-owned outputs). Host only.
+ * Returns CB_OK, or the first failing call's status with its outputs as that call leaves them (CB_E_CAPACITY:
+ * step->used, or plans[l].used for the layer that did not fit, tells the size needed; CB_E_NOSPACE from the
+ * scheduler stops before planning). CB_E_INVAL for missing pointers or meta_capacity > out_capacity.
+ */
+cb_status cb_build_step(const cb_req *reqs, int32_t n_reqs, const cb_sched_params *params,
+                        const cb_layer_pool *layers, const cb_attn_shape *shapes, int32_t *out, int64_t meta_capacity,
+                        int64_t out_capacity, cb_step *step, cb_plan *plans, int64_t *plan_offsets);
+
 /* ------------------------------------------------------------------------------------------------ cache layout */
 
 /*

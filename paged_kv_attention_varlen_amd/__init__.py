@@ -347,6 +347,16 @@ class Scheduler:
                              self.prompt_hashes)
         self.set_state(reqs, free)
 
+    def build_step_into(self, out_addr: int, meta_capacity: int, out_capacity: int, shapes, step: _abi.cb_step,
+                        plans, plan_offsets) -> None:
+        """cb_build_step: schedule into the int32 buffer at address out_addr and plan every layer (shapes: a ctypes
+        array of cb_attn_shape) into the same buffer after meta_capacity; fills `step`, `plans` (ctypes array of
+        cb_plan) and `plan_offsets` (ctypes array of int64, from meta_capacity). Raises on any status but OK."""
+        st = self._lib.cb_build_step(self.reqs, self.n, C.byref(self.params), self.pools, shapes, out_addr,
+                                     meta_capacity, out_capacity, C.byref(step), plans, plan_offsets)
+        if st != CB_OK:
+            raise CbError(st, "cb_build_step")
+
     def build_into(self, out: np.ndarray) -> _abi.cb_step:
         """Schedule into `out` (a C-contiguous int32 array); returns the header. Raises on any status but OK."""
         step = _abi.cb_step()

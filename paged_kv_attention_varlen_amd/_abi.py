@@ -72,7 +72,7 @@ class cb_attn_args(C.Structure):
                 ("timing_stop", C.c_void_p)]
 
 
-EXPORTS = ("cb_build_metadata", "cb_advance", "cb_slot_mapping", "cb_validate_metadata", "cb_plan_attention", "cb_kv_append", "cb_kv_copy_pages", "cb_paged_attention", "cb_paged_attention_noalloc",
+EXPORTS = ("cb_build_metadata", "cb_build_step", "cb_advance", "cb_slot_mapping", "cb_validate_metadata", "cb_plan_attention", "cb_kv_append", "cb_kv_copy_pages", "cb_paged_attention", "cb_paged_attention_noalloc",
            "cb_paged_attention_workspace_size", "cb_fnv1a64", "cb_block_hashes", "cb_pcache_create",
            "cb_pcache_destroy", "cb_pcache_match", "cb_pcache_lookup", "cb_pcache_allocate", "cb_pcache_commit", "cb_pcache_release",
            "cb_pcache_stats", "cb_pcache_page_info", "cb_status_str", "cb_abi_version")
@@ -98,6 +98,10 @@ def load(path: str = LIB_PATH):
     lib.cb_build_metadata.restype = C.c_int32
     lib.cb_build_metadata.argtypes = [C.POINTER(cb_req), C.c_int32, C.POINTER(cb_sched_params),
                                       C.POINTER(cb_layer_pool), i32p, C.c_int64, C.POINTER(cb_step)]
+    lib.cb_build_step.restype = C.c_int32
+    lib.cb_build_step.argtypes = [C.POINTER(cb_req), C.c_int32, C.POINTER(cb_sched_params), C.POINTER(cb_layer_pool),
+                                  C.POINTER(cb_attn_shape), C.c_void_p, C.c_int64, C.c_int64, C.POINTER(cb_step),
+                                  C.POINTER(cb_plan), C.POINTER(C.c_int64)]
     lib.cb_advance.restype = C.c_int32
     lib.cb_advance.argtypes = [C.POINTER(cb_req), C.c_int32, C.POINTER(cb_sched_params), C.POINTER(cb_layer_pool),
                                i32p, C.POINTER(cb_step), i32p, C.c_int32]

@@ -338,6 +338,31 @@ extern "C" cb_status cb_build_metadata(const cb_req *reqs, int32_t n_reqs, const
     return (N == 0 && blocked) ? CB_E_NOSPACE : CB_OK;
 }
 
+// ------------------------------------------------------------------------------------- schedule and plan at once
+
+extern "C" cb_status cb_build_step(const cb_req *reqs, int32_t n_reqs, const cb_sched_params *params,
+                                   const cb_layer_pool *layers, const cb_attn_shape *shapes, int32_t *out,
+                                   int64_t meta_capacity, int64_t out_capacity, cb_step *step, cb_plan *plans,
+                                   int64_t *plan_offsets) {
+    if (!params || !shapes || !plans || !plan_offsets || !out || !step || meta_capacity < 0 ||
+        out_capacity < meta_capacity)
+        return CB_E_INVAL;
+    const cb_status st = cb_build_metadata(reqs, n_reqs, params, layers, out, meta_capacity, step);
+    if (st != CB_OK) return st;
+    const int32_t N = step->num_reqs;
+    int64_t at = 0;
+    for (int l = 0; l < params->n_layers; ++l) {
+        const int32_t *ring = layers[l].ring_len > 0 ? out + step->off_ring_len[l] : nullptr;
+        plan_offsets[l] = at;
+        const cb_status ps = cb_plan_attention(out + step->off_query_start_loc, out + step->off_seq_lens, ring, N,
+                                               &shapes[l], out + meta_capacity + at, out_capacity - meta_capacity - at,
+                                               &plans[l]);
+        if (ps != CB_OK) return ps;
+        at += plans[l].used;
+    }
+    return CB_OK;
+}
+
 // ------------------------------------------------------------------------------------------ request lifecycle
 
 extern "C" cb_status cb_advance(cb_req *reqs, int32_t n_reqs, const cb_sched_params *params, cb_layer_pool *layers,

@@ -16,7 +16,7 @@ import numpy as np
 
 from .hip_events import HipEvent, memcpy_h2d_async
 from . import (CB_LAYOUT_KD_VT, CB_PHASE_COMBINE, CB_PHASE_DECODE, CB_PHASE_PREFILL, CB_PHASE_ROWWISE, AttnPlan,
-               CB_E_CAPACITY, CbError, Scheduler, _abi, check_dtypes, kv_append, paged_attention, plan_into,
+               CB_E_CAPACITY, CbError, Scheduler, _abi, check_dtypes, kv_append, paged_attention,
                schedule_arrays)
 
 
@@ -137,6 +137,7 @@ class StepPipeline:
         self.dtype = dt
         self.shapes = [_abi.cb_attn_shape(step.Hq, step.Hkv, step.D, step.P, dt, scheduler.windows[l], decode_split,
                                           prefill_split, prefill_rows) for l in range(self.n_layers)]
+        self._shape_arr = (_abi.cb_attn_shape * max(self.n_layers, 1))(*self.shapes)
         for L in step.layers:
             check_dtypes(AttnPlan(None, self.shapes[0], None), q=L.q, out=L.out, k_cache=L.k_cache,
                          v_cache=L.v_cache, k_new=L.k_new, v_new=L.v_new)
@@ -206,6 +207,15 @@ class StepPipeline:
         self.cap = self.meta_cap + self.plan_cap + pad_cap
         self.host = [torch.empty(self.cap, dtype=torch.int32, pin_memory=True) for _ in range(2)]
         self.dev = [torch.empty(self.cap, dtype=torch.int32, device=self.device) for _ in range(2)]
+        # per buffer pair, made once: host views and addresses, and the header and plan records cb_build_step fills
+        # (a step's records stay valid until its buffer pair is scheduled into again, two steps later)
+        L = self.n_layers
+        self._host_np = [h.numpy() for h in self.host]
+        self._host_addr = [h.data_ptr() for h in self.host]
+        self._dev_addr = [d.data_ptr() for d in self.dev]
+        self._hdr = [_abi.cb_step() for _ in range(2)]
+        self._plan_infos = [(_abi.cb_plan * max(L, 1))() for _ in range(2)]
+        self._plan_offs = [(C.c_int64 * max(L, 1))() for _ in range(2)]
         self.graphs.clear()    # captured launches point into the old buffers
 
     def _grow(self):
@@ -240,32 +250,27 @@ class StepPipeline:
         self.ws_fits[l] = info.n_partials
 
     def _host_step(self, i):
-        """Schedule and plan into pinned buffer i; with graphs=True also lay the metadata out at its padded shape.
-        Returns (header, plans, copy range lo, hi, launch views, graph key)."""
-        host = self.host[i].numpy()
-        hs = self.sched.build_into(host[:self.meta_cap])
-        N, T = hs.num_reqs, hs.num_tokens
+        """Schedule and plan into pinned buffer i (one cb_build_step call); with graphs=True also lay the metadata out
+        at its padded shape. Returns (header, plans, copy range lo, hi, launch views, graph key)."""
+        host = self._host_np[i]
+        hs, infos, offs = self._hdr[i], self._plan_infos[i], self._plan_offs[i]
+        self.sched.build_step_into(self._host_addr[i], self.meta_cap, self.meta_cap + self.plan_cap, self._shape_arr,
+                                   hs, infos, offs)
+        T = hs.num_tokens
         if T > self.rows:
             raise ValueError(f"step has {T} tokens, the step's tensors hold {self.rows}")
-        qsl = host[hs.off_query_start_loc:hs.off_query_start_loc + N + 1]
-        seq = host[hs.off_seq_lens:hs.off_seq_lens + N]
-        plan_area = host[self.meta_cap:self.meta_cap + self.plan_cap]
-        at = 0
-        plans = []
-        for l in range(self.n_layers):
-            ring = host[hs.off_ring_len[l]:hs.off_ring_len[l] + N] if self.sched.rings[l] > 0 else None
-            p = plan_into(qsl, seq, ring, self.shapes[l], plan_area[at:])
-            plans.append((p, self.meta_cap + at))
-            at += int(p.info.used)
+        L = self.n_layers
+        plans = [(AttnPlan(infos[l], self.shapes[l], None), self.meta_cap + int(offs[l])) for l in range(L)]
         if self.use_graphs:
             return (hs, plans) + self._pad(host, hs, plans, i)
-        for l, (p, _) in enumerate(plans):
-            self._check_workspace(l, p.info)
-        base = self.dev[i].data_ptr()
+        for l in range(L):
+            self._check_workspace(l, infos[l])
+        base = self._dev_addr[i]
         views = [(base + 4 * int(hs.off_block_table[l]), int(hs.table_width[l]),
-                  base + 4 * int(hs.off_slot_mapping[l]), p.info, base + 4 * off, None, T)
-                 for l, (p, off) in enumerate(plans)]
-        return hs, plans, 0, self.meta_cap + at, views, None
+                  base + 4 * int(hs.off_slot_mapping[l]), infos[l], base + 4 * off, None, T)
+                 for l, (_, off) in enumerate(plans)]
+        end = plans[-1][1] + int(infos[L - 1].used) if L else self.meta_cap
+        return hs, plans, 0, end, views, None
 
     def _pad(self, host, hs, plans, i):
         """Write the step's metadata at the addresses of its padded shape (see the class docstring): per layer the
@@ -356,10 +361,10 @@ class StepPipeline:
         self.last_header = hs
         self.last_plans = [p.info for p, _ in plans]
         if self.keep_schedule:
-            self.last_schedule = schedule_arrays(self.host[i].numpy(), hs, self.n_layers)
+            self.last_schedule = schedule_arrays(self._host_np[i], hs, self.n_layers)
         self.num_tokens = hs.num_tokens
         ev = self.copy_ev[i]
-        dst, src, nbytes = self.dev[i].data_ptr() + 4 * lo, self.host[i].data_ptr() + 4 * lo, 4 * (hi - lo)
+        dst, src, nbytes = self._dev_addr[i] + 4 * lo, self._host_addr[i] + 4 * lo, 4 * (hi - lo)
         if self.copier is not None:
             # the copy waits only for the step that last read this device buffer, then runs beside the kernels of
             # the step in flight; the compute stream waits for it before this step's first kernel
@@ -458,7 +463,7 @@ class StepPipeline:
         the next prepare(); without it every step repeats the same schedule."""
         if self._advanced == self.k:
             raise RuntimeError("advance() was already called for this step; prepare() the next step first")
-        self.sched.advance_step(self.last_header, self.host[self.cur].numpy())
+        self.sched.advance_step(self.last_header, self._host_np[self.cur])
         self._advanced = self.k
 
     def launch(self, views, events=None):

@@ -150,3 +150,45 @@ def test_split_caps_at_page_staging_limits(P):
     # below the caps a fixed split is used as given
     small = cb.plan_attention(qsl, seq, None, 32, 8, 128, P, "bf16", -1, 1024, 2048)
     assert small.info.decode_split == 1024 and small.info.prefill_split == 2048
+
+
+def test_build_step_equals_build_then_plan_per_layer():
+    """cb_build_step (schedule and plan every layer in one call) writes the same metadata and the same plans as
+    cb_build_metadata followed by cb_plan_attention per layer, for every workload; a buffer too small for the plans
+    reports CB_E_CAPACITY."""
+    import ctypes as C
+    import numpy as np
+    import paged_kv_attention_varlen_amd as cb
+    from paged_kv_attention_varlen_amd import _abi
+    from harness.device_step import scheduler_for
+    from synth import make_workload
+    for idx in (1, 2, 3, 4, 5):
+        w = make_workload(idx)
+        s = scheduler_for(w)
+        L = len(w.layers)
+        dt = _abi.CB_DTYPE_BF16 if w.dtype == "bf16" else _abi.CB_DTYPE_F32
+        shapes = [_abi.cb_attn_shape(w.Hq, w.Hkv, w.D, w.page_size, dt, lay.window_left, 0, 0, 0) for lay in w.layers]
+        meta = 1 << 20
+        buf = np.full(meta + (1 << 20), -7, dtype=np.int32)
+        hdr, plans, offs = _abi.cb_step(), (_abi.cb_plan * L)(), (C.c_int64 * L)()
+        s.build_step_into(buf.ctypes.data, meta, buf.size, (_abi.cb_attn_shape * L)(*shapes), hdr, plans, offs)
+        ref = np.full(meta, -7, dtype=np.int32)
+        rh = s.build_into(ref)
+        assert hdr.used == rh.used and np.array_equal(buf[:rh.used], ref[:rh.used]), idx
+        N = rh.num_reqs
+        qsl = ref[rh.off_query_start_loc:rh.off_query_start_loc + N + 1]
+        seq = ref[rh.off_seq_lens:rh.off_seq_lens + N]
+        for l in range(L):
+            ring = ref[rh.off_ring_len[l]:rh.off_ring_len[l] + N] if w.layers[l].ring_len > 0 else None
+            want = cb.plan_into(qsl, seq, ring, shapes[l], np.zeros(1 << 20, dtype=np.int32))
+            got = buf[meta + offs[l]:meta + offs[l] + plans[l].used]
+            assert C.string_at(C.addressof(plans[l]), C.sizeof(_abi.cb_plan)) == \
+                C.string_at(C.addressof(want.info), C.sizeof(_abi.cb_plan)), (idx, l)
+            assert np.array_equal(got, want.buffer), (idx, l)
+        small = np.zeros(rh.used + 16, dtype=np.int32)
+        try:
+            s.build_step_into(small.ctypes.data, rh.used, small.size, (_abi.cb_attn_shape * L)(*shapes), hdr, plans,
+                              offs)
+            raise AssertionError("expected CB_E_CAPACITY")
+        except cb.CbError as e:
+            assert e.status == cb.CB_E_CAPACITY
