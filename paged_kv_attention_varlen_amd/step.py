@@ -358,8 +358,9 @@ class StepPipeline:
                 else:
                     self._grow_workspace(e.layer, e.need)
         self.k += 1
-        self.last_header = hs
-        self.last_plans = [p.info for p, _ in plans]
+        # copies: the records themselves belong to the buffer pair and are rewritten two steps later
+        self.last_header = _abi.cb_step.from_buffer_copy(hs)
+        self.last_plans = [_abi.cb_plan.from_buffer_copy(p.info) for p, _ in plans]
         if self.keep_schedule:
             self.last_schedule = schedule_arrays(self._host_np[i], hs, self.n_layers)
         self.num_tokens = hs.num_tokens
