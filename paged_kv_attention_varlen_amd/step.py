@@ -426,6 +426,12 @@ class StepPipeline:
                 attend(l, CB_PHASE_DECODE, E(l, 0), E(l, 1))
             self.join.record(self.aux)
             stream.wait_event(self.join)
+        elif not events:
+            # no per-phase events: one call per layer launches its decode, per-token, prefill and merge kernels in
+            # that order (the layers are independent, so each layer's merge may precede the next layer's kernels)
+            for l in range(n):
+                attend(l, 0)
+            return
         else:
             for l in range(n):
                 attend(l, CB_PHASE_DECODE, E(l, 0), E(l, 1))
