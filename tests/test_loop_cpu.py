@@ -199,8 +199,10 @@ def test_cb_advance_checks_before_changing_anything():
                         C.byref(hdr), store.ctypes.data_as(_abi.i32p), 4)
     assert st == 1   # CB_E_INVAL
     assert sched.reqs[0].num_computed == 0 and sched.pools[0].n_free == 20
+    # the failed calls changed nothing, so the real call applies the step once: the whole 10-token prompt ran
+    # (budget 16), the request decodes next and owns ceil(10 / 4) = 3 pages, the first three of the free list
+    assert hdr.num_tokens == 10 and hdr.used_pages[0] == 3
     sched.advance_step(hdr, buf)
     r = sched.requests[0]
-    assert (r.state, r.num_computed, r.num_pending) == (PREFILLING, 10 if hdr.num_tokens == 10 else hdr.num_tokens,
-                                                        10 - hdr.num_tokens) or r.state == DECODING
-    assert sched.free_pages[0].size == 20 - hdr.used_pages[0]
+    assert (r.state, r.num_computed, r.num_pending) == (DECODING, 10, 1)
+    assert r.pages[0].tolist() == [2, 3, 4] and sched.free_pages[0].tolist() == list(range(5, 22))
