@@ -232,14 +232,19 @@ __global__ __launch_bounds__(256) void copy_pages_kernel(uint8_t *__restrict__ d
 
 constexpr int kDecodeMaxPages = 1040;   // page ids of one decode split staged in LDS (split / page + 2)
 
+// decode splits of at least this many keys run the decode kernel with one tile in flight per wave (see decode_kernel)
+constexpr int kDecodeSingleBufferSplit = 2560;
+
 template <int D>
 struct DecodeTile {
     u32x4 k[2][D / 32];   // K rows of both 16-key halves, d = 32kb + 8(l/16) .. +8
     u32x4 v[D / 16];      // V^T rows d = 16b + l%16, keys 8(l/16) .. +8
 };
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(const uint16_t *__restrict__ q, uint16_t *__restrict__ out,
+// NBUF: 32-key K/V tiles each wave holds in registers. Two (one computed while the next loads) at two work groups
+// per CU; one at three work groups per CU, which the launch picks for long splits (kDecodeSingleBufferSplit).
+template <int D, int NBUF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NBUF == 2 ? 2 : 3, NBUF == 2 ? 2 : 3))) void decode_kernel(const uint16_t *__restrict__ q, uint16_t *__restrict__ out,
                                                      const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
                                                      const int32_t *__restrict__ block_table, int table_width,
                                                      int num_pages, const int32_t *__restrict__ items,
@@ -417,19 +422,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // tiles of 32 keys, round-robin over the 4 waves; the next tile's loads are in flight while one is computed
     const int tile_last = (kv_hi - 1) >> 5;
     int tile = (kv_lo >> 5) + wave;
-    if (tile <= tile_last) {
-        DecodeTile<D> ta, tb;
-        load_tile(tile, ta);
-        while (true) {
-            const int t1 = tile + 4;
-            if (t1 <= tile_last) load_tile(t1, tb);
+    if constexpr (NBUF == 2) {
+        if (tile <= tile_last) {
+            DecodeTile<D> ta, tb;
+            load_tile(tile, ta);
+            while (true) {
+                const int t1 = tile + 4;
+                if (t1 <= tile_last) load_tile(t1, tb);
+                compute_tile(tile, ta);
+                if (t1 > tile_last) break;
+                const int t2 = t1 + 4;
+                if (t2 <= tile_last) load_tile(t2, ta);
+                compute_tile(t1, tb);
+                if (t2 > tile_last) break;
+                tile = t2;
+            }
+        }
+    } else {
+        for (; tile <= tile_last; tile += 4) {
+            DecodeTile<D> ta;
+            load_tile(tile, ta);
             compute_tile(tile, ta);
-            if (t1 > tile_last) break;
-            const int t2 = t1 + 4;
-            if (t2 <= tile_last) load_tile(t2, ta);
-            compute_tile(t1, tb);
-            if (t2 > tile_last) break;
-            tile = t2;
         }
     }
     // ---- per-wave totals, then merge the 4 waves
@@ -1202,14 +1215,23 @@ extern "C" cb_status cb_paged_attention(const cb_attn_args *a, void *stream) {
         const uint16_t *kn = append_here ? static_cast<const uint16_t *>(a->k_new) : nullptr;
         const uint16_t *vn = append_here ? static_cast<const uint16_t *>(a->v_new) : nullptr;
         const int32_t *sm = append_here ? a->slot_mapping : nullptr;
-        if (D == 128)
-            CB_LAUNCH(decode_kernel<128>, grid, dim3(256), qq, oo, kk, vv, a->block_table, a->table_width,
-                      a->num_pages, plan + pl.off_decode, part_o, part_ml, Hq, Hkv, Pl, sl2e, n_dec, kw, vw, kn, vn, sm,
-                      a->num_new, a->counts);
-        else
-            CB_LAUNCH(decode_kernel<64>, grid, dim3(256), qq, oo, kk, vv, a->block_table, a->table_width,
-                      a->num_pages, plan + pl.off_decode, part_o, part_ml, Hq, Hkv, Pl, sl2e, n_dec, kw, vw, kn, vn, sm,
-                      a->num_new, a->counts);
+        // long splits: one tile in flight per wave and three work groups per CU; short ones: two tiles per wave
+        const bool single = pl.decode_split >= kDecodeSingleBufferSplit;
+#define CB_DECODE(DD, NB)                                                                                         \
+    CB_LAUNCH((decode_kernel<DD, NB>), grid, dim3(256), qq, oo, kk, vv, a->block_table, a->table_width, a->num_pages, \
+              plan + pl.off_decode, part_o, part_ml, Hq, Hkv, Pl, sl2e, n_dec, kw, vw, kn, vn, sm, a->num_new, a->counts)
+        if (D == 128) {
+            if (single)
+                CB_DECODE(128, 1);
+            else
+                CB_DECODE(128, 2);
+        } else {
+            if (single)
+                CB_DECODE(64, 1);
+            else
+                CB_DECODE(64, 2);
+        }
+#undef CB_DECODE
     } else if (append_here) {
         // the plan's first cache reader is the per-token or the prefill kernel: append on its own launch first
         const hipError_t e = launch_append(const_cast<void *>(a->k_cache), const_cast<void *>(a->v_cache), a->k_new,

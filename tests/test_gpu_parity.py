@@ -179,6 +179,13 @@ EDGE = {
     # pages, so the 9001-key decode row and the chunk's 12.5k-key tiles each take two splits of the largest size
     "page 8 at the page-id staging limits": dict(reqs=[(DECODING, 9000, 1), (PREFILLING, 12500, 40)], P=8,
                                                  decode_split=1 << 16, prefill_split=1 << 20),
+    # decode splits of 2560 keys or more run the decode kernel with one tile in flight per wave: at the threshold,
+    # rows ending just below and at a split boundary, a short row, and head dim 64
+    "decode splits at the one-tile threshold": dict(reqs=[(DECODING, 6000, 1), (DECODING, 2559, 1),
+                                                          (DECODING, 2560, 1), (DECODING, 33, 1),
+                                                          (PREFILLING, 200, 50)], decode_split=2560),
+    "head dim 64 with long decode splits": dict(reqs=[(DECODING, 5000, 1), (DECODING, 100, 1), (WAITING, 0, 40)],
+                                                D=64, decode_split=4096),
     # the kernels' XCD mapping of (item, kv head) pairs: 16 kv heads (two per XCD) and 3 (no XCD grouping)
     "16 kv heads": dict(reqs=[(DECODING, 2000, 1), (DECODING, 300, 1), (PREFILLING, 500, 200), (WAITING, 0, 90)],
                         Hq=32, Hkv=16),
